@@ -1,0 +1,119 @@
+"""ctypes binding of the C ABI in ``include/lmhead_logps.h``.
+
+Argument marshalling only: every step of the head runs in the HIP library.
+There is no CPU fallback; loading fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblmhead_logps.so")
+
+LMH_OK = 0
+ERROR_NAMES = {
+    -1: "LMH_ERR_NULL",
+    -2: "LMH_ERR_SHAPE",
+    -3: "LMH_ERR_CHUNK",
+    -4: "LMH_ERR_WORKSPACE",
+    -5: "LMH_ERR_ARGS",
+    -6: "LMH_ERR_UNSUPPORTED",
+    -7: "LMH_ERR_HIP",
+}
+
+EXPORTED = (
+    "lmhead_logps_workspace_bytes",
+    "lmhead_logps_fwd",
+    "lmhead_logps_bwd",
+    "lmhead_logps_last_error",
+    "lmhead_logps_version",
+)
+
+
+class LmheadError(RuntimeError):
+    """A non-zero status from the library, with its name and message."""
+
+    def __init__(self, code: int, message: str):
+        self.code = code
+        self.name = ERROR_NAMES.get(code, str(code))
+        super().__init__(f"{self.name} ({code}): {message}")
+
+
+_lib = None
+
+
+def _hip_runtimes_mapped():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({l.split()[-1] for l in f if "libamdhip64" in l})
+    except OSError:  # pragma: no cover
+        return []
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and return the HIP library; raise if it is not built.
+
+    PyTorch is imported first so that the library binds to the HIP runtime
+    PyTorch already loaded (its wheel bundles one with the same soname):
+    device pointers and streams handed over from torch are only valid in
+    that runtime. A process that ends up with two HIP runtimes is refused."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: the HIP library is not built "
+            "(run `python -m cross_entropy_amd.build` or __graft_entry__.build())")
+    import torch  # noqa: F401  (binds the library to torch's HIP runtime)
+    lib = ctypes.CDLL(path)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError(f"two HIP runtimes are loaded in this process: {runtimes}")
+    i64, p, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    lib.lmhead_logps_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.POINTER(sz)]
+    lib.lmhead_logps_workspace_bytes.restype = ctypes.c_int
+    lib.lmhead_logps_fwd.argtypes = [p, p, p, i64, i64, i64, i64, p, p, p, p, sz, p]
+    lib.lmhead_logps_fwd.restype = ctypes.c_int
+    lib.lmhead_logps_bwd.argtypes = [p, p, p, i64, i64, i64, i64, p, p, p, p, p, p, p, sz, p]
+    lib.lmhead_logps_bwd.restype = ctypes.c_int
+    lib.lmhead_logps_last_error.argtypes = []
+    lib.lmhead_logps_last_error.restype = ctypes.c_char_p
+    lib.lmhead_logps_version.argtypes = []
+    lib.lmhead_logps_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def check(code: int) -> None:
+    if code != LMH_OK:
+        msg = load().lmhead_logps_last_error().decode(errors="replace")
+        raise LmheadError(code, msg)
+
+
+def raw_workspace_bytes(N: int, H: int, V: int, chunk_size: int, with_backward: bool) -> int:
+    out = ctypes.c_size_t(0)
+    check(load().lmhead_logps_workspace_bytes(int(N), int(H), int(V), int(chunk_size),
+                                              1 if with_backward else 0, ctypes.byref(out)))
+    return int(out.value)
+
+
+def raw_fwd(hidden, W, targets, N, H, V, chunk_size, logp, entropy, lse, workspace, workspace_bytes,
+            stream) -> int:
+    """Call lmhead_logps_fwd with integer addresses (0 = NULL); returns the status."""
+    return load().lmhead_logps_fwd(hidden or None, W or None, targets or None, int(N), int(H), int(V),
+                                   int(chunk_size), logp or None, entropy or None, lse or None,
+                                   workspace or None, int(workspace_bytes), stream or None)
+
+
+def raw_bwd(hidden, W, targets, N, H, V, chunk_size, lse, entropy, g_logp, g_ent, dh, dW, workspace,
+            workspace_bytes, stream) -> int:
+    """Call lmhead_logps_bwd with integer addresses (0 = NULL); returns the status."""
+    return load().lmhead_logps_bwd(hidden or None, W or None, targets or None, int(N), int(H), int(V),
+                                   int(chunk_size), lse or None, entropy or None, g_logp or None,
+                                   g_ent or None, dh or None, dW or None, workspace or None,
+                                   int(workspace_bytes), stream or None)
+
+
+def version() -> str:
+    return load().lmhead_logps_version().decode()

@@ -1,0 +1,228 @@
+// lmhead_api.hip -- the C ABI declared in include/lmhead_logps.h: argument
+// checks, work planning and launches on the caller's stream.
+//
+// Planning follows the chunked head of the pages (SkyRL issue "[tx] support
+// long sequence", "4. Chunked LM Head"; google/tunix pull request #2876,
+// the chunk loop over flattened tokens):
+//  * The forward holds no [tokens, vocab] transient. It runs one tile kernel
+//    over all tokens, with the vocabulary cut into S splits so that the
+//    launch fills the 256 CUs; S partial (max, exp-sum, exp-weighted sum,
+//    target logit) records per token are merged by log-sum-exp.
+//  * The backward holds the logits' cotangent as bf16 blocks of Ct tokens x
+//    Vb vocabulary entries. chunk_size bounds the block: Ct * Vb * 2 bytes
+//    stays within one float32 [chunk_size, V] tensor, the transient the
+//    pages' chunked head holds per chunk. Within that bound the block shape
+//    is chosen to cut the dh / dW accumulation traffic and launch tails.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/lmhead_logps.h"
+#include "lmhead_internal.h"
+
+namespace lmh {
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+FwdPlan plan_forward(int64_t N, int64_t H, int64_t V) {
+  (void)H;
+  FwdPlan p;
+  p.n_tt = (int)ceil_div(N, kTileRows);
+  p.n_vt = (int)ceil_div(V, kTileRows);
+  const int s_max = (int)std::min<int64_t>(p.n_vt, 128);
+  // makespan in tile-steps: rounds of resident workgroups x tiles per split
+  auto cost = [&](int S) {
+    return ceil_div((int64_t)p.n_tt * S, kNumCUs) * ceil_div(p.n_vt, S);
+  };
+  int64_t best = INT64_MAX;
+  for (int S = 1; S <= s_max; ++S) best = std::min(best, cost(S));
+  // among near-best split counts, prefer S near 8: 32 concurrent workgroups
+  // of an XCD then cover 4 token tiles x 8 vocabulary tiles and share L2.
+  int pick = 1;
+  double pick_dist = 1e30;
+  for (int S = 1; S <= s_max; ++S) {
+    if ((double)cost(S) > 1.03 * (double)best) continue;
+    const double dist = std::fabs(std::log2((double)S / 8.0));
+    if (dist < pick_dist) {
+      pick_dist = dist;
+      pick = S;
+    }
+  }
+  p.S = std::max(1, pick);
+  p.part_ld = round_up(std::max<int64_t>(N, 1), 64);
+  p.bytes = (size_t)round_up((int64_t)p.S * p.part_ld * 16, 256);
+  return p;
+}
+
+BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, int64_t chunk_size) {
+  const int64_t T = kTileRows;
+  N = std::max<int64_t>(N, 1);
+  // bf16 elements of the dz block: at most chunk_size * V * 4 bytes, and at
+  // least one 256 x 256 tile.
+  const double budget = std::max<double>((double)chunk_size * (double)V * 2.0, (double)(T * T));
+  const int64_t n_pad = round_up(std::max<int64_t>(N, 1), T);
+  const int64_t v_pad = round_up(V, T);
+  const int64_t n_ht = ceil_div(H, T);
+  // model constants: per-CU bf16 MFMA rate at a realistic efficiency, HBM
+  // rate for the f32 accumulation traffic, per-launch cost
+  const double rate = 2.5e15 * 0.6 / kNumCUs;
+  const double hbm = 5.0e12;
+  const double launch = 6e-6;
+
+  BwdPlan best;
+  double best_t = 1e300;
+  for (int64_t ct = T; ct <= n_pad; ct += T) {
+    int64_t vb = (int64_t)(budget / (double)ct) / T * T;
+    vb = std::min(vb, v_pad);
+    if (vb < T) break;
+    const int64_t n_tb = ceil_div(N, ct);
+    const int64_t n_vb = ceil_div(V, vb);
+    const int64_t c2 = round_up(ceil_div(N, n_tb), T);   // even out the blocks
+    const int64_t v2 = round_up(ceil_div(V, n_vb), T);
+    const double tile_dz = 2.0 * T * T * (double)H / rate;
+    const double n3 = (double)(c2 / T) * (double)(v2 / T);
+    const double t3 = std::ceil(n3 / kNumCUs) * tile_dz;
+    const double tile_dw = 2.0 * T * T * (double)c2 / rate;
+    const double tile_dh = 2.0 * T * T * (double)v2 / rate;
+    const double work45 = (double)(v2 / T) * n_ht * tile_dw + (double)(c2 / T) * n_ht * tile_dh;
+    const double t45 = work45 / kNumCUs + 0.5 * std::max(tile_dw, tile_dh);
+    const double traffic = (8.0 * N * H * n_vb + 8.0 * V * H * n_tb) / hbm * 0.3;
+    const double t = (double)(n_tb * n_vb) * (t3 + t45 + 2 * launch) + traffic;
+    if (t < best_t) {
+      best_t = t;
+      best.Ct = c2;
+      best.Vb = v2;
+      best.n_tb = n_tb;
+      best.n_vb = n_vb;
+    }
+  }
+  best.ld = best.Vb;
+  best.bytes = (size_t)round_up(best.Ct * best.Vb * 2, 256);
+  return best;
+}
+
+}  // namespace lmh
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return LMH_OK;
+}
+
+int check_shape(int64_t N, int64_t H, int64_t V, int64_t chunk_size) {
+  if (N < 0 || N >= (int64_t(1) << 31))
+    return fail(LMH_ERR_SHAPE, "N must be in [0, 2^31), got %lld", (long long)N);
+  if (H <= 0 || H >= (int64_t(1) << 20))
+    return fail(LMH_ERR_SHAPE, "H must be in (0, 2^20), got %lld", (long long)H);
+  if (V <= 0 || V >= (int64_t(1) << 31))
+    return fail(LMH_ERR_SHAPE, "V must be in (0, 2^31), got %lld", (long long)V);
+  if (chunk_size <= 0) return fail(LMH_ERR_CHUNK, "chunk_size must be > 0, got %lld", (long long)chunk_size);
+  if (H % 64 != 0) return fail(LMH_ERR_UNSUPPORTED, "H must be a multiple of 64, got %lld", (long long)H);
+  return LMH_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* lmhead_logps_last_error(void) { return g_last_error.c_str(); }
+
+const char* lmhead_logps_version(void) { return "lmhead_logps 0.1.0 (gfx950)"; }
+
+int lmhead_logps_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t chunk_size,
+                                 int with_backward, size_t* bytes_out) {
+  if (bytes_out == nullptr) return fail(LMH_ERR_NULL, "bytes_out is NULL");
+  const int rc = check_shape(N, H, V, chunk_size);
+  if (rc != LMH_OK) return rc;
+  size_t b = lmh::plan_forward(N, H, V).bytes;
+  if (with_backward) b = std::max(b, lmh::plan_backward(N, H, V, chunk_size).bytes);
+  *bytes_out = b;
+  return ok();
+}
+
+int lmhead_logps_fwd(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, int64_t N,
+                     int64_t H, int64_t V, int64_t chunk_size, float* logp, float* entropy,
+                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(N, H, V, chunk_size);
+  if (rc != LMH_OK) return rc;
+  if (N == 0) return ok();
+  if (!hidden || !W || !targets || !logp || !lse || !workspace)
+    return fail(LMH_ERR_NULL, "fwd: hidden, W, targets, logp, lse and workspace must be non-NULL");
+  if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(workspace, 16) || !aligned(targets, 4) ||
+      !aligned(logp, 4) || !aligned(lse, 4) || (entropy && !aligned(entropy, 4)))
+    return fail(LMH_ERR_UNSUPPORTED, "fwd: hidden, W and workspace need 16-byte alignment");
+  const lmh::FwdPlan p = lmh::plan_forward(N, H, V);
+  if (workspace_bytes < p.bytes)
+    return fail(LMH_ERR_WORKSPACE, "fwd: workspace of %zu bytes, %zu needed", workspace_bytes, p.bytes);
+  lmh::FwdArgs a{hidden, W, targets, N, H, V, p.S, p.n_tt, p.n_vt, workspace, p.part_ld,
+                 logp, entropy, lse};
+  const hipError_t e = lmh::launch_fwd(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LMH_ERR_HIP, "fwd: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int lmhead_logps_bwd(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, int64_t N,
+                     int64_t H, int64_t V, int64_t chunk_size, const float* lse,
+                     const float* entropy, const float* g_logp, const float* g_ent, float* dh,
+                     float* dW, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(N, H, V, chunk_size);
+  if (rc != LMH_OK) return rc;
+  if (g_ent != nullptr && entropy == nullptr)
+    return fail(LMH_ERR_ARGS, "bwd: g_ent given without the forward's entropy");
+  if (!dW) return fail(LMH_ERR_NULL, "bwd: dW must be non-NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0) {
+    const hipError_t e = lmh::launch_fill_zero(dW, V * H, s);
+    if (e != hipSuccess) return fail(LMH_ERR_HIP, "bwd: launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
+  if (!hidden || !W || !targets || !lse || !dh || !workspace)
+    return fail(LMH_ERR_NULL, "bwd: hidden, W, targets, lse, dh, dW and workspace must be non-NULL");
+  if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(workspace, 16) || !aligned(dh, 4) ||
+      !aligned(dW, 4))
+    return fail(LMH_ERR_UNSUPPORTED, "bwd: hidden, W and workspace need 16-byte alignment");
+  const lmh::BwdPlan p = lmh::plan_backward(N, H, V, chunk_size);
+  if (workspace_bytes < p.bytes)
+    return fail(LMH_ERR_WORKSPACE, "bwd: workspace of %zu bytes, %zu needed", workspace_bytes, p.bytes);
+  lmh::BwdArgs a{hidden, W, targets, N, H, V, lse, entropy, g_logp, g_ent, dh, dW,
+                 static_cast<uint16_t*>(workspace), p.ld};
+  for (int64_t tb = 0; tb < p.n_tb; ++tb) {
+    for (int64_t vb = 0; vb < p.n_vb; ++vb) {
+      lmh::BwdBlock b;
+      b.t0 = tb * p.Ct;
+      b.Ct = std::min(p.Ct, N - b.t0);
+      b.v0 = vb * p.Vb;
+      b.Vb = std::min(p.Vb, V - b.v0);
+      b.acc_dh = vb > 0;
+      b.acc_dW = tb > 0;
+      if (b.Ct <= 0 || b.Vb <= 0) continue;
+      const hipError_t e = lmh::launch_bwd_block(a, b, s);
+      if (e != hipSuccess) return fail(LMH_ERR_HIP, "bwd: launch failed: %s", hipGetErrorString(e));
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

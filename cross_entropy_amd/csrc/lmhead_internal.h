@@ -1,0 +1,74 @@
+// lmhead_internal.h -- launch descriptors shared by the C ABI (lmhead_api.hip)
+// and the kernels (lmhead_kernels.hip). Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lmh {
+
+constexpr int kTileRows = 256;   // output tile edge of every MMA kernel
+constexpr int kNumCUs = 256;     // MI355X: 8 XCDs x 32 CUs
+
+// Forward: token tiles x vocabulary splits of the tile kernel, then the merge.
+struct FwdPlan {
+  int n_tt = 0;          // token tiles of 256
+  int n_vt = 0;          // vocabulary tiles of 256
+  int S = 0;             // vocabulary splits (partials per token)
+  int64_t part_ld = 0;   // tokens per split row of the partials array
+  size_t bytes = 0;      // workspace bytes (partials)
+};
+
+// Backward: the token x vocabulary plane is cut into blocks of at most
+// Ct x Vb; one bf16 dz block buffer of Ct_pad x ld is reused for every block.
+struct BwdPlan {
+  int64_t Ct = 0, Vb = 0;      // block edges (tokens, vocabulary), multiples of 256
+  int64_t n_tb = 0, n_vb = 0;  // blocks along tokens and vocabulary
+  int64_t ld = 0;              // dz row stride (= Vb)
+  size_t bytes = 0;            // dz buffer bytes
+};
+
+FwdPlan plan_forward(int64_t N, int64_t H, int64_t V);
+BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, int64_t chunk_size);
+
+struct FwdArgs {
+  const uint16_t* hidden;
+  const uint16_t* W;
+  const int32_t* targets;
+  int64_t N, H, V;
+  int S, n_tt, n_vt;
+  void* part;
+  int64_t part_ld;
+  float* logp;
+  float* entropy;
+  float* lse;
+};
+
+struct BwdArgs {
+  const uint16_t* hidden;
+  const uint16_t* W;
+  const int32_t* targets;
+  int64_t N, H, V;
+  const float* lse;
+  const float* entropy;
+  const float* g_logp;
+  const float* g_ent;
+  float* dh;
+  float* dW;
+  uint16_t* dz;
+  int64_t ld_dz;
+};
+
+struct BwdBlock {
+  int64_t t0, Ct;   // tokens [t0, t0 + Ct)
+  int64_t v0, Vb;   // vocabulary [v0, v0 + Vb)
+  int acc_dh;       // 0: first vocabulary block writes dh, 1: adds
+  int acc_dW;       // 0: first token block writes dW, 1: adds
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_block(const BwdArgs& a, const BwdBlock& b, hipStream_t stream);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+
+}  // namespace lmh

@@ -1,0 +1,143 @@
+/*
+ * lmhead_logps.h -- C ABI of the fused LM-head log-prob and entropy head
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Per token i with hidden row h_i and target id t_i the head computes, over
+ * the whole vocabulary and without ever holding the [tokens, vocab] logits:
+ *
+ *   z      = W h_i                                  (logits, V values)
+ *   lse    = log sum_v exp(z_v)
+ *   logp   = z[t_i] - lse
+ *   entropy= lse - sum_v softmax(z)_v z_v           (nats)
+ *
+ * and, for a loss L = sum_i g_logp_i logp_i + g_ent_i entropy_i, the
+ * gradients dh = dL/dh and dW = dL/dW through
+ *
+ *   dz = g_logp (onehot(t) - p) - g_ent p (log p + entropy),  p = softmax(z)
+ *   dh_i = W^T dz_i,   dW = sum_i dz_i h_i^T.
+ *
+ * Definitions follow the pages this library is built from:
+ *  - SkyRL issue "[tx] support long sequence", "4. Chunked LM Head": the
+ *    cross-entropy of the LM head is computed chunk by chunk so the full
+ *    logits tensor is never held (10 GB -> about 300 MB at chunk 512).
+ *  - google/tunix pull request #2913, the fused sharded log-prob head: one
+ *    pass over a chunk's logits gives the target logit by a one-hot select,
+ *    the max and exp-sum once and the entropy from the same exponentials;
+ *    the backward forms the logits' cotangent in one elementwise pass over
+ *    recomputed logits, and both gradient matmuls read that one cotangent;
+ *    a loss that differentiates the entropy adds the entropy term. Ids are
+ *    valid iff 0 <= id < vocab.
+ *  - google/tunix pull request #2876: the chunk loop over flattened tokens,
+ *    int32 targets in, float32 log-probs (and entropies) out, results that
+ *    do not depend on the chunk size beyond float32 summation order.
+ *
+ * Conventions for every entry point
+ *  - Pointers are device memory owned by the caller (e.g. allocated by
+ *    PyTorch), row-major, 16-byte aligned. bf16 values are passed as their
+ *    16-bit patterns (uint16_t).
+ *  - Shapes: N >= 0 tokens, H > 0 hidden with H % 64 == 0, 0 < V < 2^31.
+ *  - chunk_size > 0 counts flattened tokens. It bounds the backward's
+ *    transient memory: the logits cotangent the backward holds at any time is
+ *    at most one float32 [chunk_size, V] tensor in bytes (it is kept as bf16
+ *    blocks of tokens x vocabulary). The forward holds no [tokens, vocab]
+ *    transient at all. Per-token forward results do not depend on
+ *    chunk_size; gradients depend on it only through float32 summation order.
+ *  - Targets outside [0, V) (-1 included) mask the token: its logp, entropy
+ *    and lse are written as 0, its dh row is written as 0 and it adds nothing
+ *    to dW, whatever its hidden row holds (NaN and inf included). They are
+ *    not errors.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    default stream). The library never synchronises the device, allocates
+ *    no device memory and keeps no state between calls: distinct workspaces
+ *    on distinct streams may be used from several threads at once.
+ *  - Outputs are overwritten in full (dW is not accumulated into).
+ *  - Return value: LMH_OK (0) or a negative LMH_ERR_* code. Argument checks
+ *    run on the host before anything is enqueued, so a failing call enqueues
+ *    nothing. lmhead_logps_last_error() gives a thread-local message for the
+ *    last failing call of the calling thread.
+ */
+#ifndef LMHEAD_LOGPS_H_
+#define LMHEAD_LOGPS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LMH_OK 0
+#define LMH_ERR_NULL (-1)        /* a required pointer is NULL */
+#define LMH_ERR_SHAPE (-2)       /* N < 0, H <= 0, V <= 0 or V >= 2^31 */
+#define LMH_ERR_CHUNK (-3)       /* chunk_size <= 0 */
+#define LMH_ERR_WORKSPACE (-4)   /* workspace smaller than the queried size */
+#define LMH_ERR_ARGS (-5)        /* g_ent given without entropy */
+#define LMH_ERR_UNSUPPORTED (-6) /* H % 64 != 0, or a misaligned pointer */
+#define LMH_ERR_HIP (-7)         /* a HIP call or kernel launch failed */
+
+/*
+ * Bytes of device workspace a call needs. with_backward = 0 sizes the
+ * forward only; with_backward != 0 sizes a workspace that serves both the
+ * forward and the backward (one buffer may be reused for both calls when
+ * they run in stream order). Pure host computation, no device call.
+ * Errors: LMH_ERR_NULL (bytes_out), LMH_ERR_SHAPE, LMH_ERR_CHUNK.
+ */
+int lmhead_logps_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t chunk_size,
+                                 int with_backward, size_t* bytes_out);
+
+/*
+ * Forward: logp, entropy and lse per token (SkyRL "4. Chunked LM Head";
+ * tunix #2913 one-pass scoring of logits).
+ *   hidden   bf16 [N, H]   token hidden states
+ *   W        bf16 [V, H]   output embedding (vocabulary) table
+ *   targets  int32 [N]     target ids; outside [0, V) masks the token
+ *   logp     f32 [N]       out: z[t] - lse, 0 when masked
+ *   entropy  f32 [N]       out, or NULL when not requested; 0 when masked
+ *   lse      f32 [N]       out: log-sum-exp of the logits, 0 when masked
+ *   workspace / workspace_bytes: device scratch of at least
+ *            lmhead_logps_workspace_bytes(N, H, V, chunk_size, 0) bytes;
+ *            its contents on entry are ignored.
+ * Errors: LMH_ERR_NULL (hidden, W, targets, logp, lse, or workspace when
+ * N > 0), LMH_ERR_SHAPE, LMH_ERR_CHUNK, LMH_ERR_WORKSPACE, LMH_ERR_UNSUPPORTED,
+ * LMH_ERR_HIP. N = 0 enqueues nothing and returns LMH_OK.
+ */
+int lmhead_logps_fwd(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
+                     int64_t N, int64_t H, int64_t V, int64_t chunk_size,
+                     float* logp, float* entropy, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward: dh and dW of L = sum_i g_logp_i logp_i + g_ent_i entropy_i
+ * (tunix #2913: the cotangent of the recomputed logits in one elementwise
+ * pass, read by both gradient matmuls; the entropy term when the entropy is
+ * differentiated).
+ *   hidden, W, targets, N, H, V, chunk_size: as for the forward
+ *   lse      f32 [N]       the forward's lse output (required)
+ *   entropy  f32 [N]       the forward's entropy output; required iff g_ent
+ *   g_logp   f32 [N]       cotangent of logp, or NULL for all zeros
+ *   g_ent    f32 [N]       cotangent of entropy, or NULL for all zeros
+ *   dh       f32 [N, H]    out, overwritten; masked rows are 0
+ *   dW       f32 [V, H]    out, overwritten (not accumulated into)
+ *   workspace: at least lmhead_logps_workspace_bytes(..., 1) bytes.
+ * Errors: LMH_ERR_NULL, LMH_ERR_SHAPE, LMH_ERR_CHUNK, LMH_ERR_WORKSPACE,
+ * LMH_ERR_ARGS (g_ent without entropy), LMH_ERR_UNSUPPORTED, LMH_ERR_HIP.
+ * N = 0 writes dW = 0 and returns LMH_OK.
+ */
+int lmhead_logps_bwd(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
+                     int64_t N, int64_t H, int64_t V, int64_t chunk_size,
+                     const float* lse, const float* entropy,
+                     const float* g_logp, const float* g_ent,
+                     float* dh, float* dW,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Thread-local message of the calling thread's last failing call ("" if none). */
+const char* lmhead_logps_last_error(void);
+
+/* Library version string. */
+const char* lmhead_logps_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMHEAD_LOGPS_H_ */

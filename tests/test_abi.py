@@ -1,0 +1,132 @@
+"""The C-ABI library on the host: it loads, exports every function the public
+header declares, and rejects bad arguments with the documented codes before
+touching the GPU (no compute call runs here). Fake device addresses are
+used only on paths that fail validation."""
+import json
+import os
+import re
+
+import pytest
+
+from cross_entropy_amd import _native as nat
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lmhead_logps.h")
+
+FAKE = 0x10000        # 64 KiB-aligned non-NULL address; never dereferenced
+MIS = FAKE + 2        # misaligned address
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lmhead_logps_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = nat.load()
+    names = declared_functions()
+    assert set(names) == set(nat.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert "gfx950" in nat.version()
+
+
+def test_error_codes_match_header():
+    src = open(HEADER).read()
+    codes = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (LMH_ERR_\w+) \((-\d+)\)", src)}
+    assert codes == {v: k for k, v in nat.ERROR_NAMES.items()}
+
+
+def _fwd(**kw):
+    a = dict(hidden=FAKE, W=FAKE, targets=FAKE, N=64, H=128, V=300, chunk_size=16, logp=FAKE, entropy=FAKE,
+             lse=FAKE, workspace=FAKE, workspace_bytes=0, stream=0)
+    a.update(kw)
+    return nat.raw_fwd(**a)
+
+
+def _bwd(**kw):
+    a = dict(hidden=FAKE, W=FAKE, targets=FAKE, N=64, H=128, V=300, chunk_size=16, lse=FAKE, entropy=FAKE,
+             g_logp=FAKE, g_ent=FAKE, dh=FAKE, dW=FAKE, workspace=FAKE, workspace_bytes=0, stream=0)
+    a.update(kw)
+    return nat.raw_bwd(**a)
+
+
+@pytest.mark.parametrize("call", [_fwd, _bwd])
+def test_shape_and_chunk_errors(call):
+    assert call(N=-1) == -2
+    assert call(H=0) == -2
+    assert call(V=0) == -2
+    assert call(V=1 << 31) == -2
+    assert call(N=1 << 31) == -2
+    assert call(chunk_size=0) == -3
+    assert call(chunk_size=-5) == -3
+    assert call(H=96) == -6
+    assert "multiple of 64" in nat.load().lmhead_logps_last_error().decode()
+
+
+def test_forward_null_alignment_and_workspace_errors():
+    for k in ("hidden", "W", "targets", "logp", "lse", "workspace"):
+        assert _fwd(**{k: 0}) == -1, k
+    assert _fwd(hidden=MIS) == -6
+    assert _fwd(W=MIS) == -6
+    assert _fwd(workspace=MIS) == -6
+    need = nat.raw_workspace_bytes(64, 128, 300, 16, False)
+    assert _fwd(workspace_bytes=need - 1) == -4
+    assert "needed" in nat.load().lmhead_logps_last_error().decode()
+    assert _fwd(N=0, hidden=0, W=0, targets=0, logp=0, lse=0, workspace=0) == 0   # N = 0: nothing to do
+
+
+def test_backward_null_args_alignment_and_workspace_errors():
+    assert _bwd(entropy=0) == -5           # g_ent without the forward's entropy
+    assert _bwd(dW=0) == -1
+    for k in ("hidden", "W", "targets", "lse", "dh", "workspace"):
+        assert _bwd(**{k: 0}) == -1, k
+    assert _bwd(hidden=MIS) == -6
+    need = nat.raw_workspace_bytes(64, 128, 300, 16, True)
+    assert _bwd(workspace_bytes=need - 1) == -4
+
+
+def test_workspace_query_errors():
+    import ctypes
+    assert nat.load().lmhead_logps_workspace_bytes(1, 64, 10, 4, 0, None) == -1
+    with pytest.raises(nat.LmheadError) as e:
+        nat.raw_workspace_bytes(1, 65, 10, 4, True)
+    assert e.value.code == -6
+    assert nat.raw_workspace_bytes(0, 64, 10, 4, True) > 0
+    _ = ctypes
+
+
+SHAPES = [(256, 256, 4096, 128), (4096, 2560, 151936, 512), (65536, 2560, 151936, 512),
+          (15237, 4096, 151936, 1024), (15237, 4096, 151936, 4096), (65536, 2560, 151936, 4096),
+          (700, 320, 3001, 7), (1, 64, 1, 1)]
+
+
+@pytest.mark.parametrize("N,H,V,C", SHAPES)
+def test_backward_transient_within_one_f32_chunk_of_logits(N, H, V, C):
+    """The backward's [tokens, vocab]-shaped transient stays within one
+    float32 [chunk_size, V] tensor (at least one 256 x 256 bf16 tile); the
+    forward's workspace is O(N), independent of V."""
+    b = nat.raw_workspace_bytes(N, H, V, C, True)
+    f = nat.raw_workspace_bytes(N, H, V, C, False)
+    assert b <= max(C * V * 4, 256 * 256 * 2) + f + 256
+    assert f <= 16 * 128 * max(64, (N + 63) // 64 * 64) + 256
+
+
+def test_pages_chunk_512_figure():
+    """At the pages' headline shape (batch 16 x 4k tokens, 152k vocabulary,
+    chunk 512) the backward transient is at most the ~300 MB of one float32
+    [512, vocab] chunk of logits (SkyRL "[tx] support long sequence",
+    "4. Chunked LM Head")."""
+    f = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_figures.json")))["chunked_lm_head_memory"]
+    b = nat.raw_workspace_bytes(f["batch"] * f["seq_len"], 2560, f["vocab"], f["chunk_size"], True)
+    assert b <= f["chunk_size"] * f["vocab"] * 4
+    assert b / 1e6 < 1.05 * f["chunked_MB"] + 11.2
+
+
+def test_library_binds_to_one_hip_runtime():
+    """The binding imports torch before loading the library, so the process
+    holds a single HIP runtime (torch's), whose pointers and streams the
+    library is handed."""
+    nat.load()
+    assert len(nat._hip_runtimes_mapped()) == 1
