@@ -9,10 +9,14 @@
 //    launch fills the 256 CUs; S partial (max, exp-sum, exp-weighted sum,
 //    target logit) records per token are merged by log-sum-exp.
 //  * The backward holds the logits' cotangent as bf16 blocks of Ct tokens x
-//    Vb vocabulary entries. chunk_size bounds the block: Ct * Vb * 2 bytes
-//    stays within one float32 [chunk_size, V] tensor, the transient the
-//    pages' chunked head holds per chunk. Within that bound the block shape
-//    is chosen to cut the dh / dW accumulation traffic and launch tails.
+//    Vb vocabulary entries, twice (token-major for the dh GEMM and
+//    vocabulary-major for the dW GEMM). chunk_size bounds the block: the two
+//    copies, 4 bytes per element, stay within one float32 [chunk_size, V]
+//    tensor, the transient the pages' chunked head holds per chunk. Within
+//    that bound the block shape is chosen to cut the dh / dW accumulation
+//    traffic and launch tails. The workspace also holds bf16 transposes of W
+//    and of the hidden states (input-sized), so every GEMM operand is
+//    K-contiguous.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -63,9 +67,9 @@ FwdPlan plan_forward(int64_t N, int64_t H, int64_t V) {
 BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, int64_t chunk_size) {
   const int64_t T = kTileRows;
   N = std::max<int64_t>(N, 1);
-  // bf16 elements of the dz block: at most chunk_size * V * 4 bytes, and at
-  // least one 256 x 256 tile.
-  const double budget = std::max<double>((double)chunk_size * (double)V * 2.0, (double)(T * T));
+  // elements of the dz block (held as two bf16 copies, 4 bytes each): at
+  // most chunk_size * V, and at least one 256 x 256 tile.
+  const double budget = std::max<double>((double)chunk_size * (double)V, (double)(T * T));
   const int64_t n_pad = round_up(std::max<int64_t>(N, 1), T);
   const int64_t v_pad = round_up(V, T);
   const int64_t n_ht = ceil_div(H, T);
@@ -102,8 +106,15 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, int64_t chunk_size) {
       best.n_vb = n_vb;
     }
   }
-  best.ld = best.Vb;
-  best.bytes = (size_t)round_up(best.Ct * best.Vb * 2, 256);
+  best.N_pad = round_up(N, T);
+  best.V_pad = round_up(V, T);
+  best.H_pad = round_up(H, T);
+  const size_t one = (size_t)round_up(best.Ct * best.Vb * 2, 256);
+  best.dz_bytes = 2 * one;
+  best.off_dzt = one;
+  best.off_wt = 2 * one;
+  best.off_ht = best.off_wt + (size_t)round_up(best.H_pad * best.V_pad * 2, 256);
+  best.bytes = best.off_ht + (size_t)round_up(best.H_pad * best.N_pad * 2, 256);
   return best;
 }
 
@@ -206,8 +217,16 @@ int lmhead_logps_bwd(const uint16_t* hidden, const uint16_t* W, const int32_t* t
   const lmh::BwdPlan p = lmh::plan_backward(N, H, V, chunk_size);
   if (workspace_bytes < p.bytes)
     return fail(LMH_ERR_WORKSPACE, "bwd: workspace of %zu bytes, %zu needed", workspace_bytes, p.bytes);
+  char* ws = static_cast<char*>(workspace);
   lmh::BwdArgs a{hidden, W, targets, N, H, V, lse, entropy, g_logp, g_ent, dh, dW,
-                 static_cast<uint16_t*>(workspace), p.ld};
+                 reinterpret_cast<uint16_t*>(ws), p.Vb,
+                 reinterpret_cast<uint16_t*>(ws + p.off_dzt), p.Ct,
+                 reinterpret_cast<uint16_t*>(ws + p.off_wt), p.V_pad,
+                 reinterpret_cast<uint16_t*>(ws + p.off_ht), p.N_pad};
+  hipError_t te = lmh::launch_transpose(W, H, V, H, p.V_pad, p.H_pad, nullptr, V, a.Wt, p.V_pad, s);
+  if (te == hipSuccess)
+    te = lmh::launch_transpose(hidden, H, N, H, p.N_pad, p.H_pad, targets, V, a.ht, p.N_pad, s);
+  if (te != hipSuccess) return fail(LMH_ERR_HIP, "bwd: launch failed: %s", hipGetErrorString(te));
   for (int64_t tb = 0; tb < p.n_tb; ++tb) {
     for (int64_t vb = 0; vb < p.n_vb; ++vb) {
       lmh::BwdBlock b;

@@ -21,12 +21,16 @@ struct FwdPlan {
 };
 
 // Backward: the token x vocabulary plane is cut into blocks of at most
-// Ct x Vb; one bf16 dz block buffer of Ct_pad x ld is reused for every block.
+// Ct x Vb; the block's cotangent is held twice in bf16 (dz [Ct][Vb] and
+// dzt [Vb][Ct]), i.e. 4 bytes per element like one float32 block. The
+// workspace also holds W^T [H_pad][V_pad] and hidden^T [H_pad][N_pad].
 struct BwdPlan {
   int64_t Ct = 0, Vb = 0;      // block edges (tokens, vocabulary), multiples of 256
   int64_t n_tb = 0, n_vb = 0;  // blocks along tokens and vocabulary
-  int64_t ld = 0;              // dz row stride (= Vb)
-  size_t bytes = 0;            // dz buffer bytes
+  int64_t N_pad = 0, V_pad = 0, H_pad = 0;
+  size_t off_dzt = 0, off_wt = 0, off_ht = 0;   // byte offsets in the workspace
+  size_t dz_bytes = 0;         // dz + dzt
+  size_t bytes = 0;            // total
 };
 
 FwdPlan plan_forward(int64_t N, int64_t H, int64_t V);
@@ -56,8 +60,14 @@ struct BwdArgs {
   const float* g_ent;
   float* dh;
   float* dW;
-  uint16_t* dz;
+  uint16_t* dz;      // [Ct][Vb] block, row stride ld_dz
   int64_t ld_dz;
+  uint16_t* dzt;     // [Vb][Ct] block, row stride ld_dzt
+  int64_t ld_dzt;
+  uint16_t* Wt;      // W^T [H_pad][V_pad]
+  int64_t ld_wt;
+  uint16_t* ht;      // hidden^T [H_pad][N_pad], masked tokens zeroed
+  int64_t ld_ht;
 };
 
 struct BwdBlock {
@@ -70,5 +80,8 @@ struct BwdBlock {
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_block(const BwdArgs& a, const BwdBlock& b, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+hipError_t launch_transpose(const uint16_t* in, int64_t ld_in, int64_t R, int64_t C, int64_t R_pad,
+                            int64_t C_pad, const int32_t* tgt, int64_t V, uint16_t* out,
+                            int64_t ld_out, hipStream_t stream);
 
 }  // namespace lmh

@@ -12,12 +12,14 @@
 //             gradient matmuls (dh = dz W, dW = dz^T h) read that one dz.
 //
 // Every contraction runs on one MFMA tile core: a 256 x 256 output tile per
-// 512-thread workgroup (8 wave64s as 2 x 4, each owning 128 x 64), K staged
-// through LDS in double-buffered 64-deep slices, v_mfma_f32_32x32x16_bf16.
-// Operands are either K-contiguous (loaded with 16-byte vector loads) or
-// MN-contiguous (loaded as 8 x 4 blocks and transposed in registers with
-// byte permutes before the LDS write), so no operand is ever copied into a
-// transposed buffer.
+// 512-thread workgroup (8 wave64s as 2 x 4, each owning 128 x 64),
+// v_mfma_f32_32x32x16_bf16, with both operands K-contiguous. K is staged
+// through a 4-deep ring of 32-wide LDS slices filled by direct-to-LDS loads
+// (global_load_lds_dwordx4), so three slices are in flight while one is
+// consumed and no VGPRs hold staged data. Slice rows are 64 bytes with a
+// 16-byte-chunk XOR swizzle, which keeps the MFMA fragment reads free of
+// bank conflicts. Operands that are stored MN-contiguous (W and hidden in
+// the backward) are given to the core through transposed copies.
 //
 // MFMA 32x32x16 register layout used throughout (wave64): lane l supplies
 // row (l % 32) of A and column (l % 32) of B with the 8 K values
@@ -36,16 +38,17 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 512;
-constexpr int kTile = 256;                 // BM = BN
-constexpr int kBK = 64;                    // K slice per LDS stage
-constexpr int kRowBytes = kBK * 2 + 16;    // 128 data bytes + 16 pad: conflict-free 16 B reads
-constexpr int kTileBytes = kTile * kRowBytes;
-constexpr int kStageBytes = 2 * kTileBytes;
-constexpr int kLdsBytes = 2 * kStageBytes; // 147,456 B of the 160 KB per CU
+constexpr int kTile = 256;                       // output tile edge
+constexpr int kBK = 32;                          // K per LDS slice
+constexpr int kStages = 4;                       // slices in the ring
+constexpr int kRowBytes = kBK * 2;               // 64 B per staged row
+constexpr int kOpBytes = kTile * kRowBytes;      // 16 KB per operand slice
+constexpr int kStageBytes = 2 * kOpBytes;        // A + B
+constexpr int kLdsBytes = kStages * kStageBytes; // 128 KB of the 160 KB per CU
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr float kNegBig = -1.0e30f;        // "minus infinity" that keeps 0 * x finite
+constexpr float kNegBig = -1.0e30f;              // "minus infinity" that keeps 0 * x finite
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -53,6 +56,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v = {lo, hi};
   bf16x2 b = __builtin_convertvector(v, bf16x2);   // round to nearest even
   return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+  return (uint16_t)(pack_bf16x2(x, 0.0f) & 0xFFFFu);
 }
 
 // Workgroup id -> virtual id such that each XCD (workgroups are dealt to the
@@ -76,112 +83,58 @@ __device__ __forceinline__ void raster(int vid, int n_m, int n_n, int group, int
 }
 
 // ---------------------------------------------------------------------------
-// Operand loaders. Each stages one [256 rows x 64 K] slice into LDS as
-// rows of 64 K values (128 B) padded to kRowBytes.
-
-// K-contiguous operand: element (row, k) at base[row * ld + k].
-struct LoadK {
+// Staging. A K-contiguous operand: element (row, k) at base[row * ld + k];
+// rows at or past `rows` read row rows-1 instead (their results are
+// discarded or masked by the epilogues), so every load stays in bounds.
+struct Operand {
   const uint16_t* base;
   int64_t ld;
-  int rows;          // rows of this tile that exist; others load as 0
-  uint4 r[4];
-
-  __device__ __forceinline__ void load(int k0) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = tid + kThreads * j;
-      const int row = idx >> 3;
-      const int ch = idx & 7;
-      if (row < rows) {
-        r[j] = *reinterpret_cast<const uint4*>(base + (int64_t)row * ld + k0 + ch * 8);
-      } else {
-        r[j] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(char* lds) const {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = tid + kThreads * j;
-      const int row = idx >> 3;
-      const int ch = idx & 7;
-      *reinterpret_cast<uint4*>(lds + row * kRowBytes + ch * 16) = r[j];
-    }
-  }
+  int rows;
 };
 
-// MN-contiguous operand: element (row, k) at base[k * ld + row]. Each thread
-// loads 8 K-rows x 4 columns (8-byte loads) and transposes them in registers
-// into 4 rows of 8 consecutive K values. K-rows at or beyond k_valid load as
-// 0; with `tgt` set, K-rows whose target id lies outside [0, V) load as 0 too
-// (masked tokens: their hidden rows never reach a product, whatever they hold).
-struct LoadMN {
-  const uint16_t* base;
-  int64_t ld;
-  int k_valid;
-  int cols;          // columns (rows of the staged tile) that exist, multiple of 4
-  const int32_t* tgt;
-  int V;
-  uint2 r[8];
+// 16-byte chunk index of logical chunk c of staged row r.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-  __device__ __forceinline__ void load(int k0) {
-    const int tid = threadIdx.x;
-    const int kg = tid & 7;
-    const int cg = tid >> 3;
-    const bool col_ok = cg * 4 < cols;
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// One direct-to-LDS load: 64 lanes x 16 B land at m0 + 16 * lane. Issued as
+// inline asm so the compiler does not add a vmcnt(0) in front of every LDS
+// read of the ring; completion is awaited explicitly (wait_vm) before the
+// barrier that publishes a slice.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_wave_base)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(n) leaving expcnt / lgkmcnt alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Stage rows [0, 256) x K [k0, k0 + 32) of one operand. Each wave loads 32
+// rows as 2 x 16 rows of 4 chunks; lane l fills physical chunk l % 4 of row
+// l / 4 with the logical chunk that the swizzle puts there.
+__device__ __forceinline__ void stage(const Operand& op, int k0, uint32_t lds_op) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int k = k0 + kg * 8 + q;
-      bool ok = col_ok && (k < k_valid);
-      if (tgt != nullptr && ok) {
-        const int t = tgt[k];
-        ok = (t >= 0) && (t < V);
-      }
-      if (ok) {
-        r[q] = *reinterpret_cast<const uint2*>(base + (int64_t)k * ld + cg * 4);
-      } else {
-        r[q] = make_uint2(0u, 0u);
-      }
-    }
+  for (int q = 0; q < 2; ++q) {
+    const int r = wave * 32 + q * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz(r);
+    const int rr = min(r, op.rows - 1);
+    const uint16_t* g = op.base + (int64_t)rr * op.ld + k0 + c * 8;
+    dma16(g, __builtin_amdgcn_readfirstlane(lds_op + (wave * 32 + q * 16) * kRowBytes));
   }
-  __device__ __forceinline__ void store(char* lds) const {
-    const int tid = threadIdx.x;
-    const int kg = tid & 7;
-    const int cg = tid >> 3;
-    // column c of the 8 x 4 block: word w packs K-rows 2w (low) and 2w+1 (high)
-    uint4 o0, o1, o2, o3;
-    o0.x = __builtin_amdgcn_perm(r[1].x, r[0].x, 0x05040100u);
-    o0.y = __builtin_amdgcn_perm(r[3].x, r[2].x, 0x05040100u);
-    o0.z = __builtin_amdgcn_perm(r[5].x, r[4].x, 0x05040100u);
-    o0.w = __builtin_amdgcn_perm(r[7].x, r[6].x, 0x05040100u);
-    o1.x = __builtin_amdgcn_perm(r[1].x, r[0].x, 0x07060302u);
-    o1.y = __builtin_amdgcn_perm(r[3].x, r[2].x, 0x07060302u);
-    o1.z = __builtin_amdgcn_perm(r[5].x, r[4].x, 0x07060302u);
-    o1.w = __builtin_amdgcn_perm(r[7].x, r[6].x, 0x07060302u);
-    o2.x = __builtin_amdgcn_perm(r[1].y, r[0].y, 0x05040100u);
-    o2.y = __builtin_amdgcn_perm(r[3].y, r[2].y, 0x05040100u);
-    o2.z = __builtin_amdgcn_perm(r[5].y, r[4].y, 0x05040100u);
-    o2.w = __builtin_amdgcn_perm(r[7].y, r[6].y, 0x05040100u);
-    o3.x = __builtin_amdgcn_perm(r[1].y, r[0].y, 0x07060302u);
-    o3.y = __builtin_amdgcn_perm(r[3].y, r[2].y, 0x07060302u);
-    o3.z = __builtin_amdgcn_perm(r[5].y, r[4].y, 0x07060302u);
-    o3.w = __builtin_amdgcn_perm(r[7].y, r[6].y, 0x07060302u);
-    char* p = lds + (cg * 4) * kRowBytes + kg * 16;
-    *reinterpret_cast<uint4*>(p) = o0;
-    *reinterpret_cast<uint4*>(p + kRowBytes) = o1;
-    *reinterpret_cast<uint4*>(p + 2 * kRowBytes) = o2;
-    *reinterpret_cast<uint4*>(p + 3 * kRowBytes) = o3;
-  }
-};
+}
 
-// ---------------------------------------------------------------------------
 // The tile core: acc[i][j] (wave sub-block i of 32 A-rows, j of 32 B-rows)
-// = sum over k < K of A[row][k] * B[col][k]. K is a multiple of 64.
-// Ends with a barrier, so LDS may be reused right after it returns.
-template <class LA, class LB>
-__device__ __forceinline__ void mma_tile(LA& la, LB& lb, int K, char* lds, f32x16 (&acc)[4][2]) {
+// = sum over k < K of A[row][k] * B[row][k]. K is a multiple of 32. Ends
+// with a barrier, so LDS may be reused as soon as it returns.
+__device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int K, char* lds,
+                                         f32x16 (&acc)[4][2]) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1;
@@ -193,45 +146,55 @@ __device__ __forceinline__ void mma_tile(LA& la, LB& lb, int K, char* lds, f32x1
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  const uint32_t base = lds_offset(lds);
   const int nk = K / kBK;
-  la.load(0);
-  lb.load(0);
-  la.store(lds);
-  lb.store(lds + kTileBytes);
-  __syncthreads();
-
-  const int a_off = (wm * 128 + (lane & 31)) * kRowBytes + (lane >> 5) * 16;
-  const int b_off = kTileBytes + (wn * 64 + (lane & 31)) * kRowBytes + (lane >> 5) * 16;
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) {
+    if (s < nk) {
+      stage(A, s * kBK, base + s * kStageBytes);
+      stage(B, s * kBK, base + s * kStageBytes + kOpBytes);
+    }
+  }
+  const int sw = swz(lane & 31);
+  const int a_off = (wm * 128 + (lane & 31)) * kRowBytes;
+  const int b_off = kOpBytes + (wn * 64 + (lane & 31)) * kRowBytes;
 
   for (int kt = 0; kt < nk; ++kt) {
-    const char* cur = lds + (kt & 1) * kStageBytes;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load((kt + 1) * kBK);
-      lb.load((kt + 1) * kBK);
+    // this wave's loads of slice kt are done once at most the later slices'
+    // 4 loads each are outstanding; the barrier then publishes everybody's
+    const int later = min(kStages - 2, nk - 1 - kt);
+    if (later >= 2) {
+      wait_vm<8>();
+    } else if (later == 1) {
+      wait_vm<4>();
+    } else {
+      wait_vm<0>();
     }
+    __syncthreads();
+    if (kt + kStages - 1 < nk) {
+      const uint32_t st = base + ((kt + kStages - 1) % kStages) * kStageBytes;
+      stage(A, (kt + kStages - 1) * kBK, st);
+      stage(B, (kt + kStages - 1) * kBK, st + kOpBytes);
+    }
+    const char* cur = lds + (kt % kStages) * kStageBytes;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int co = (((ks * 2) + (lane >> 5)) ^ sw) * 16;
       bf16x8 a[4], b[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(cur + a_off + i * 32 * kRowBytes + ks * 32);
+        a[i] = *reinterpret_cast<const bf16x8*>(cur + a_off + i * 32 * kRowBytes + co);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(cur + b_off + j * 32 * kRowBytes + ks * 32);
+        b[j] = *reinterpret_cast<const bf16x8*>(cur + b_off + j * 32 * kRowBytes + co);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      char* nxt = lds + ((kt + 1) & 1) * kStageBytes;
-      la.store(nxt);
-      lb.store(nxt + kTileBytes);
-    }
-    __syncthreads();
   }
+  __syncthreads();
 }
 
 // Row (within the wave's 128 rows) held by register r of sub-block i.
@@ -291,12 +254,12 @@ __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
     st[j].zt = 0.0f;
   }
 
-  LoadK lb{hidden + (int64_t)tok0 * H, H, min(kTile, N - tok0)};
+  const Operand ob{hidden + (int64_t)tok0 * H, H, min(kTile, N - tok0)};
   for (int vt = s; vt < n_vt; vt += S) {
     const int v0 = vt * kTile;
-    LoadK la{W + (int64_t)v0 * H, H, min(kTile, V - v0)};
+    const Operand oa{W + (int64_t)v0 * H, H, min(kTile, V - v0)};
     f32x16 acc[4][2];
-    mma_tile(la, lb, H, lds, acc);
+    mma_tile(oa, ob, H, lds, acc);
 
     const int vrow0 = v0 + wm * 128;
     if (vrow0 + 128 > V) {   // ragged last tile: rows past V take no part
@@ -403,16 +366,18 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(
 // Backward, step 1: recompute a logits tile of the block [t0, t0+Ct) x
 // [v0, v0+Vb) and write its cotangent
 //   dz = g_l (onehot - p) - g_e p (log p + entropy),  p = 2^(z log2e - lse log2e)
-// as bf16 into the block buffer dz[token - t0][vocab - v0] (row stride ld).
-// Rows/columns outside the block, masked tokens and vocabulary past V are
-// written as 0, so the gradient GEMMs can run over the padded block.
+// as bf16 twice: dz[token - t0][vocab - v0] (row stride ld) for the dh GEMM
+// and dzt[vocab - v0][token - t0] (row stride ldt) for the dW GEMM, so both
+// read a K-contiguous operand. Rows/columns outside the block, masked tokens
+// and vocabulary past V are written as 0, so the gradient GEMMs can run over
+// the padded block.
 __global__ __launch_bounds__(kThreads) void bwd_dz_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W,
     const int32_t* __restrict__ targets, int V, int H,
     const float* __restrict__ lse, const float* __restrict__ entropy,
     const float* __restrict__ g_logp, const float* __restrict__ g_ent,
     int t0, int Ct, int v0, int Vb, int n_tt, int n_vt,
-    uint16_t* __restrict__ dz, int64_t ld) {
+    uint16_t* __restrict__ dz, int64_t ld, uint16_t* __restrict__ dzt, int64_t ldt) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const int vid = xcd_remap(blockIdx.x, gridDim.x);
   if (vid >= n_tt * n_vt) return;
@@ -425,10 +390,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dz_kernel(
   const int tl0 = tt * kTile;   // token offset in the block
   const int vl0 = vt * kTile;   // vocabulary offset in the block
 
-  LoadK la{W + (int64_t)(v0 + vl0) * H, H, min(kTile, Vb - vl0)};
-  LoadK lb{hidden + (int64_t)(t0 + tl0) * H, H, min(kTile, Ct - tl0)};
+  const Operand oa{W + (int64_t)(v0 + vl0) * H, H, min(kTile, Vb - vl0)};
+  const Operand ob{hidden + (int64_t)(t0 + tl0) * H, H, min(kTile, Ct - tl0)};
   f32x16 acc[4][2];
-  mma_tile(la, lb, H, lds, acc);
+  mma_tile(oa, ob, H, lds, acc);
 
   float nlseL[2], c0[2], c1[2], gl[2];
   int tr[2];
@@ -443,23 +408,23 @@ __global__ __launch_bounds__(kThreads) void bwd_dz_kernel(
     live[j] = (t >= 0) && (t < V);
     const float L = live[j] ? lse[tok] : 0.0f;
     const float Hn = (live[j] && entropy != nullptr) ? entropy[tok] : 0.0f;
-    const float a = (live[j] && g_logp != nullptr) ? g_logp[tok] : 0.0f;
-    const float b = (live[j] && g_ent != nullptr) ? g_ent[tok] : 0.0f;
+    const float ga = (live[j] && g_logp != nullptr) ? g_logp[tok] : 0.0f;
+    const float gb = (live[j] && g_ent != nullptr) ? g_ent[tok] : 0.0f;
     nlseL[j] = -L * kLog2e;
-    c0[j] = -(a + b * Hn);       // dz = p * (c1 * d + c0) - ... with d = log2 p
-    c1[j] = -(b * kLn2);
-    gl[j] = a;
+    c0[j] = -(ga + gb * Hn);     // dz = p * (c1 * d + c0) (+ g_l at the target), d = log2 p
+    c1[j] = -(gb * kLn2);
+    gl[j] = ga;
     tr[j] = live[j] ? (t - v0 - vw0) : -1;
   }
   const bool any_dead = __any(!live[0] || !live[1]);
   const bool ragged = (vw0 + 128 > Vb);
 
-  uint16_t* out = dz + vw0;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int tl = tl0 + wn * 64 + j * 32 + (lane & 31);
     const bool hit_any = __any(tr[j] >= 0 && tr[j] < 128);
-    uint16_t* row = out + (int64_t)tl * ld;
+    uint16_t* row = dz + (int64_t)tl * ld + vw0;
+    uint16_t* col = dzt + (int64_t)vw0 * ldt + tl;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -479,23 +444,30 @@ __global__ __launch_bounds__(kThreads) void bwd_dz_kernel(
         uint2 w;
         w.x = pack_bf16x2(v[0], v[1]);
         w.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(row + i * 32 + 8 * g + 4 * (lane >> 5)) = w;
+        const int m = i * 32 + 8 * g + 4 * (lane >> 5);
+        *reinterpret_cast<uint2*>(row + m) = w;
+        col[(int64_t)(m + 0) * ldt] = (uint16_t)(w.x & 0xFFFFu);
+        col[(int64_t)(m + 1) * ldt] = (uint16_t)(w.x >> 16);
+        col[(int64_t)(m + 2) * ldt] = (uint16_t)(w.y & 0xFFFFu);
+        col[(int64_t)(m + 3) * ldt] = (uint16_t)(w.y >> 16);
       }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Backward, step 2: both gradient GEMMs of one block in one launch.
-//   dW tiles (first, the longer ones): dW[v0 + m][n] (+)= sum_k dz[k][m] h[t0 + k][n]
-//   dh tiles: dh[t0 + m][n] (+)= sum_k dz[m][k] W[v0 + k][n]
-// `acc_dW` / `acc_dh` select accumulate-into (later blocks) or overwrite
-// (first block of the fixed block order), which keeps the sums deterministic.
+// Backward, step 2: both gradient GEMMs of one block in one launch, all
+// operands K-contiguous.
+//   dW tiles (first, the longer ones): dW[v0 + m][n] (+)= sum_k dzt[m][k] ht[n][t0 + k]
+//   dh tiles: dh[t0 + m][n] (+)= sum_k dz[m][k] Wt[n][v0 + k]
+// ht = hidden^T with masked tokens zeroed, Wt = W^T. `acc_dW` / `acc_dh`
+// select accumulate-into (later blocks) or overwrite (first block of the
+// fixed block order), which keeps the sums deterministic.
 __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(
-    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W,
-    const int32_t* __restrict__ targets, int N, int H, int V,
-    int t0, int Ct, int v0, int Vb, const uint16_t* __restrict__ dz, int64_t ld,
-    int n_ht, int n_dw, int n_dh, float* __restrict__ dh, float* __restrict__ dW,
-    int acc_dh, int acc_dW) {
+    const uint16_t* __restrict__ ht, int64_t ld_ht, const uint16_t* __restrict__ Wt, int64_t ld_wt,
+    const int32_t* __restrict__ targets, int H, int V, int t0, int Ct, int v0, int Vb,
+    const uint16_t* __restrict__ dz, int64_t ld, const uint16_t* __restrict__ dzt, int64_t ldt,
+    int n_ht, int n_dw, int n_dh, float* __restrict__ dh, float* __restrict__ dW, int acc_dh,
+    int acc_dW) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const int vid = xcd_remap(blockIdx.x, gridDim.x);
   if (vid >= n_dw + n_dh) return;
@@ -506,14 +478,13 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(
   f32x16 acc[4][2];
 
   if (vid < n_dw) {
-    int mt, ht;
-    raster(vid, n_dw / n_ht, n_ht, 4, mt, ht);
+    int mt, hb;
+    raster(vid, n_dw / n_ht, n_ht, 4, mt, hb);
     const int m0 = mt * kTile;
-    const int h0 = ht * kTile;
-    LoadMN la{dz + m0, ld, Ct, kTile, nullptr, V};
-    LoadMN lb{hidden + (int64_t)t0 * H + h0, H, Ct, min(kTile, H - h0), targets + t0, V};
-    const int K = (Ct + kBK - 1) / kBK * kBK;
-    mma_tile(la, lb, K, lds, acc);
+    const int h0 = hb * kTile;
+    const Operand oa{dzt + (int64_t)m0 * ldt, ldt, kTile};
+    const Operand ob{ht + (int64_t)h0 * ld_ht + t0, ld_ht, kTile};
+    mma_tile(oa, ob, (Ct + kBK - 1) / kBK * kBK, lds, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -530,14 +501,13 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(
         }
       }
   } else {
-    int mt, ht;
-    raster(vid - n_dw, n_dh / n_ht, n_ht, 4, mt, ht);
+    int mt, hb;
+    raster(vid - n_dw, n_dh / n_ht, n_ht, 4, mt, hb);
     const int m0 = mt * kTile;
-    const int h0 = ht * kTile;
-    LoadK la{dz + (int64_t)m0 * ld, ld, kTile};
-    LoadMN lb{W + (int64_t)v0 * H + h0, H, Vb, min(kTile, H - h0), nullptr, V};
-    const int K = (Vb + kBK - 1) / kBK * kBK;
-    mma_tile(la, lb, K, lds, acc);
+    const int h0 = hb * kTile;
+    const Operand oa{dz + (int64_t)m0 * ld, ld, kTile};
+    const Operand ob{Wt + (int64_t)h0 * ld_wt + v0, ld_wt, kTile};
+    mma_tile(oa, ob, (Vb + kBK - 1) / kBK * kBK, lds, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -558,7 +528,56 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(
         }
       }
   }
-  (void)N;
+}
+
+// Transposed bf16 copy: out[c][r] = in[r][c] for r < R and c < C, 0 for the
+// padding r in [R, R_pad) and c in [C, C_pad); with `tgt`, rows whose target
+// id lies outside [0, V) are 0 too (masked tokens never reach the dW GEMM,
+// whatever their hidden row holds: the select happens here, once).
+// Grid: (R_pad / 64, C_pad / 64), 256 threads; 64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void transpose_kernel(
+    const uint16_t* __restrict__ in, int64_t ld_in, int R, int C, const int32_t* __restrict__ tgt,
+    int V, uint16_t* __restrict__ out, int64_t ld_out) {
+  __shared__ uint32_t t[64][33];   // 64 rows x 64 bf16 (as 32 words) + 1 word pad
+  const int r0 = blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  {
+    const int rl = tid >> 2;          // 0..63
+    const int cq = (tid & 3) * 16;    // 16 columns each
+    const int r = r0 + rl;
+    bool ok = (r < R) && (c0 + cq < C);
+    if (ok && tgt != nullptr) {
+      const int tv = tgt[r];
+      ok = (tv >= 0) && (tv < V);
+    }
+    uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = make_uint4(0u, 0u, 0u, 0u);
+    if (ok) {
+      const uint4* src = reinterpret_cast<const uint4*>(in + (int64_t)r * ld_in + c0 + cq);
+      v0 = src[0];
+      v1 = src[1];
+    }
+    uint32_t* d = &t[rl][cq >> 1];
+    d[0] = v0.x; d[1] = v0.y; d[2] = v0.z; d[3] = v0.w;
+    d[4] = v1.x; d[5] = v1.y; d[6] = v1.z; d[7] = v1.w;
+  }
+  __syncthreads();
+  {
+    const int cl = tid >> 2;          // output row (input column) 0..63
+    const int rq = (tid & 3) * 16;    // 16 input rows each
+    uint32_t w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t a = t[rq + 2 * e][cl >> 1];
+      const uint32_t b = t[rq + 2 * e + 1][cl >> 1];
+      const uint32_t lo = (cl & 1) ? (a >> 16) : (a & 0xFFFFu);
+      const uint32_t hi = (cl & 1) ? (b >> 16) : (b & 0xFFFFu);
+      w[e] = lo | (hi << 16);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(out + (int64_t)(c0 + cl) * ld_out + r0 + rq);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -590,16 +609,25 @@ hipError_t launch_bwd_block(const BwdArgs& a, const BwdBlock& b, hipStream_t str
   const int n_vt = (int)((b.Vb + kTile - 1) / kTile);
   hipLaunchKernelGGL(bwd_dz_kernel, dim3(round8((long long)n_tt * n_vt)), dim3(kThreads), 0, stream,
                      a.hidden, a.W, a.targets, (int)a.V, (int)a.H, a.lse, a.entropy, a.g_logp,
-                     a.g_ent, (int)b.t0, (int)b.Ct, (int)b.v0, (int)b.Vb, n_tt, n_vt, a.dz, a.ld_dz);
+                     a.g_ent, (int)b.t0, (int)b.Ct, (int)b.v0, (int)b.Vb, n_tt, n_vt, a.dz, a.ld_dz,
+                     a.dzt, a.ld_dzt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_ht = (int)((a.H + kTile - 1) / kTile);
   const int n_dw = n_vt * n_ht;
   const int n_dh = n_tt * n_ht;
   hipLaunchKernelGGL(bwd_grad_kernel, dim3(round8((long long)n_dw + n_dh)), dim3(kThreads), 0,
-                     stream, a.hidden, a.W, a.targets, (int)a.N, (int)a.H, (int)a.V, (int)b.t0,
-                     (int)b.Ct, (int)b.v0, (int)b.Vb, a.dz, a.ld_dz, n_ht, n_dw, n_dh, a.dh, a.dW,
-                     b.acc_dh, b.acc_dW);
+                     stream, a.ht, a.ld_ht, a.Wt, a.ld_wt, a.targets, (int)a.H, (int)a.V,
+                     (int)b.t0, (int)b.Ct, (int)b.v0, (int)b.Vb, a.dz, a.ld_dz, a.dzt, a.ld_dzt,
+                     n_ht, n_dw, n_dh, a.dh, a.dW, b.acc_dh, b.acc_dW);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const uint16_t* in, int64_t ld_in, int64_t R, int64_t C, int64_t R_pad,
+                            int64_t C_pad, const int32_t* tgt, int64_t V, uint16_t* out,
+                            int64_t ld_out, hipStream_t stream) {
+  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)(R_pad / 64), (unsigned)(C_pad / 64)), dim3(256),
+                     0, stream, in, ld_in, (int)R, (int)C, tgt, (int)V, out, ld_out);
   return hipGetLastError();
 }
 
