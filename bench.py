@@ -1,0 +1,195 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused LM-head log-prob + entropy head on one MI355X.
+
+One step = the whole hot path over one batch: the forward (logits tiles with
+running max / exp-sum / exp-weighted sum and target select, split merge)
+and the backward (logits recompute, cotangent blocks, dh and dW GEMMs) at
+the batch-16 x 4096-token Qwen3-4B-shaped head: N = 65,536 tokens,
+H = 2,560, V = 151,936, chunk_size = 512. Inputs are seeded synthetic data
+(hidden ~ N(0,1) scaled to RMS 1, W ~ N(0, 0.02), uniform targets,
+cotangents g_logp ~ N(0,1), g_ent ~ N(0,0.1)), resident in HBM before the
+timed region starts.
+
+Prints one JSON line: whole-job tokens/s, the credited MFMA throughput
+(6 N H V flops per step) as a fraction of the bf16 dense peak, a roofline
+entry for the dominant kernel (its average launch duration measured live
+with HIP events through the library's tracing, on the stream the kernels run
+on), and the fp64 CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 5] [--warmup 2]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused LM-head logp+entropy fwd+bwd tokens/s and % bf16 MFMA peak, H=2560 V=151936"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+WORKLOAD_INDEX = 3            # batch 16 x 4096 tokens
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(h_bits, W_bits, targets, chunk, g_l, g_e, sample: int):
+    """The fp64 oracle, as it stands, on `sample` tokens of the same inputs
+    (forward + backward of those tokens; dW over them)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle.lmhead_oracle as O
+    from synthetic import sample_tokens
+
+    idx = sample_tokens(targets, sample, seed=11)
+    gl = np.zeros_like(g_l)
+    ge = np.zeros_like(g_e)
+    gl[idx], ge[idx] = g_l[idx], g_e[idx]
+    t0 = time.perf_counter()
+    O.forward_backward(h_bits, W_bits, targets, chunk, gl, ge, tokens=idx)
+    dt = time.perf_counter() - t0
+    threads = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    return {
+        "value": round(idx.size / dt, 3),
+        "unit": "tokens/s",
+        "cores": int(max(threads) if threads else 1),
+        "kind": "oracle",
+        "sample": f"{idx.size} sampled tokens of the N=65536 workload, fp64 forward+backward "
+                  f"(full logits row per token, dW over the sample), {dt:.1f} s",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--cpu-sample", type=int, default=192, help="tokens the CPU oracle runs on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this head runs on a single MI355X and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import cross_entropy_amd as lm
+    from cross_entropy_amd import _native
+    from synthetic import CONFIGS, make_cotangents, make_inputs
+
+    cfg = CONFIGS[WORKLOAD_INDEX]
+    N, H, V, C = cfg.N, cfg.H, cfg.V, cfg.chunk_size
+    lm.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating workload {cfg.name}: N={N} H={H} V={V} chunk={C}")
+    h_bits, W_bits, targets = make_inputs(cfg)
+    g_l, g_e = make_cotangents(cfg)
+
+    h = torch.from_numpy(h_bits.view(np.int16)).to(dev)
+    W = torch.from_numpy(W_bits.view(np.int16)).to(dev)
+    t = torch.from_numpy(targets).to(dev)
+    gl = torch.from_numpy(g_l).to(dev)
+    ge = torch.from_numpy(g_e).to(dev)
+    logp = torch.empty(N, dtype=torch.float32, device=dev)
+    ent = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    dh = torch.empty((N, H), dtype=torch.float32, device=dev)
+    dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+    ws = lm.workspace_for(h, W, C, with_backward=True)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        lm.lmhead_logps_fwd(h, W, t, C, logp, ent, lse, ws, stream)
+        lm.lmhead_logps_bwd(h, W, t, C, lse, ent, gl, ge, dh, dW, ws, stream)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    _native.trace_enable(True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        lm.lmhead_logps_fwd(h, W, t, C, logp, ent, lse, ws, stream)
+        e1.record(stream)
+        lm.lmhead_logps_bwd(h, W, t, C, lse, ent, gl, ge, dh, dW, ws, stream)
+        e2.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernels = _native.trace_read()
+    _native.trace_enable(False)
+    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
+    bwd_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
+    if not (np.all(np.isfinite(lse.cpu().numpy())) and bool(torch.isfinite(dW).all())):
+        log("[bench] non-finite outputs")
+        return 1
+
+    ms_step = elapsed * 1e3 / args.steps
+    credited = 6.0 * N * H * V
+    executed = 8.0 * N * H * V
+    tflops = credited / (ms_step * 1e-3) / 1e12
+
+    dom_name, dom = max(kernels.items(), key=lambda kv: kv[1]["ms"])
+    avg_ms = dom["ms"] / max(1, dom["launches"])
+    if dom["flops"] > 0:
+        achieved = dom["flops"] / max(1, dom["launches"]) / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    else:
+        achieved = dom["bytes"] / max(1, dom["launches"]) / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    roof["kernel"] = dom_name
+    roof["avg_launch_ms"] = round(avg_ms, 4)
+    roof["launches_per_step"] = dom["launches"] / args.steps
+
+    out = {
+        "metric": METRIC,
+        "value": round(N * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "N": N, "H": H, "V": V, "chunk_size": C, "batch": 16,
+                   "seq_len": 4096, "parallelism": "none (one GPU)"},
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "tflops_credited": round(tflops, 1),
+        "tflops_executed": round(executed / (ms_step * 1e-3) / 1e12, 1),
+        "fwd_ms": round(fwd_ms, 3),
+        "bwd_ms": round(bwd_ms, 3),
+        "roofline": roof,
+        "kernels": {k: {"launches": v["launches"] // args.steps, "ms_per_step": round(v["ms"] / args.steps, 3)}
+                    for k, v in kernels.items() if v["launches"]},
+    }
+    if args.no_cpu_baseline:
+        out["cpu_baseline"] = None
+    else:
+        log(f"[bench] CPU oracle on {args.cpu_sample} sampled tokens")
+        out["cpu_baseline"] = cpu_baseline(h_bits, W_bits, targets, C, g_l, g_e, args.cpu_sample)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -28,6 +28,9 @@ EXPORTED = (
     "lmhead_logps_bwd",
     "lmhead_logps_last_error",
     "lmhead_logps_version",
+    "lmhead_logps_trace_enable",
+    "lmhead_logps_trace_read",
+    "lmhead_logps_trace_kernel_name",
 )
 
 
@@ -81,6 +84,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lmhead_logps_last_error.restype = ctypes.c_char_p
     lib.lmhead_logps_version.argtypes = []
     lib.lmhead_logps_version.restype = ctypes.c_char_p
+    lib.lmhead_logps_trace_enable.argtypes = [ctypes.c_int]
+    lib.lmhead_logps_trace_enable.restype = ctypes.c_int
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.lmhead_logps_trace_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int64), dp, dp, dp]
+    lib.lmhead_logps_trace_read.restype = ctypes.c_int
+    lib.lmhead_logps_trace_kernel_name.argtypes = [ctypes.c_int]
+    lib.lmhead_logps_trace_kernel_name.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -113,6 +123,28 @@ def raw_bwd(hidden, W, targets, N, H, V, chunk_size, lse, entropy, g_logp, g_ent
                                    int(chunk_size), lse or None, entropy or None, g_logp or None,
                                    g_ent or None, dh or None, dW or None, workspace or None,
                                    int(workspace_bytes), stream or None)
+
+
+TRACE_KERNELS = ("fwd_stats_kernel", "fwd_merge_kernel", "bwd_dz_kernel", "bwd_grad_kernel",
+                 "transpose_kernel", "fill_zero_kernel")
+
+
+def trace_enable(on: bool) -> None:
+    check(load().lmhead_logps_trace_enable(1 if on else 0))
+
+
+def trace_read() -> dict:
+    """{kernel name: {launches, ms, flops, bytes}} of the launches recorded
+    since tracing was enabled (waits for them to finish)."""
+    lib = load()
+    out = {}
+    for k in range(len(TRACE_KERNELS)):
+        n = ctypes.c_int64(0)
+        ms, fl, by = ctypes.c_double(0), ctypes.c_double(0), ctypes.c_double(0)
+        check(lib.lmhead_logps_trace_read(k, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl), ctypes.byref(by)))
+        out[lib.lmhead_logps_trace_kernel_name(k).decode()] = {
+            "launches": int(n.value), "ms": ms.value, "flops": fl.value, "bytes": by.value}
+    return out
 
 
 def version() -> str:

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "liblmhead_logps.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["lmhead_api.hip", "lmhead_kernels.hip"]
+SOURCES = ["lmhead_api.hip", "lmhead_kernels.hip", "lmhead_trace.hip"]
 HEADERS = ["lmhead_internal.h", os.path.join("..", "..", "include", "lmhead_logps.h")]
 
 # Packed-fp32 VALU ops are kept out of the generated code on purpose.

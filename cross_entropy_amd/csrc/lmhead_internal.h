@@ -77,6 +77,11 @@ struct BwdBlock {
   int acc_dW;       // 0: first token block writes dW, 1: adds
 };
 
+// Kernel ids of the tracing facility (lmhead_trace.hip).
+enum KernelId { kFwdStats = 0, kFwdMerge, kBwdDz, kBwdGrad, kTranspose, kFill, kNumKernels };
+void trace_begin(hipStream_t stream);
+void trace_end(int kernel, hipStream_t stream, double flops, double bytes);
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_block(const BwdArgs& a, const BwdBlock& b, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);

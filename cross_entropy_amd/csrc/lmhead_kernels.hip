@@ -593,26 +593,37 @@ static inline unsigned round8(long long x) { return (unsigned)((x + 7) / 8 * 8);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   const long long wg = (long long)a.n_tt * a.S;
+  const double N = (double)a.N, H = (double)a.H, V = (double)a.V;
+  trace_begin(stream);
   hipLaunchKernelGGL(fwd_stats_kernel, dim3(round8(wg)), dim3(kThreads), 0, stream, a.hidden, a.W,
                      a.targets, (int)a.N, (int)a.H, (int)a.V, a.S, a.n_tt, a.n_vt,
                      reinterpret_cast<float4*>(a.part), a.part_ld);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  trace_end(kFwdStats, stream, 2.0 * N * H * V, 2.0 * (N + V) * H + 4.0 * N + 16.0 * a.S * N);
+  trace_begin(stream);
   hipLaunchKernelGGL(fwd_merge_kernel, dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, stream,
                      reinterpret_cast<const float4*>(a.part), a.part_ld, a.S, a.targets, (int)a.N,
                      (int)a.V, a.logp, a.entropy, a.lse);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  trace_end(kFwdMerge, stream, 0.0, 16.0 * a.S * N + 16.0 * N);
+  return hipSuccess;
 }
 
 hipError_t launch_bwd_block(const BwdArgs& a, const BwdBlock& b, hipStream_t stream) {
   const int n_tt = (int)((b.Ct + kTile - 1) / kTile);
   const int n_vt = (int)((b.Vb + kTile - 1) / kTile);
+  const double ct = (double)b.Ct, vb = (double)b.Vb, H = (double)a.H;
+  trace_begin(stream);
   hipLaunchKernelGGL(bwd_dz_kernel, dim3(round8((long long)n_tt * n_vt)), dim3(kThreads), 0, stream,
                      a.hidden, a.W, a.targets, (int)a.V, (int)a.H, a.lse, a.entropy, a.g_logp,
                      a.g_ent, (int)b.t0, (int)b.Ct, (int)b.v0, (int)b.Vb, n_tt, n_vt, a.dz, a.ld_dz,
                      a.dzt, a.ld_dzt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  trace_end(kBwdDz, stream, 2.0 * ct * vb * H, 2.0 * (ct + vb) * H + 4.0 * ct * vb + 20.0 * ct);
+  trace_begin(stream);
   const int n_ht = (int)((a.H + kTile - 1) / kTile);
   const int n_dw = n_vt * n_ht;
   const int n_dh = n_tt * n_ht;
@@ -620,23 +631,35 @@ hipError_t launch_bwd_block(const BwdArgs& a, const BwdBlock& b, hipStream_t str
                      stream, a.ht, a.ld_ht, a.Wt, a.ld_wt, a.targets, (int)a.H, (int)a.V,
                      (int)b.t0, (int)b.Ct, (int)b.v0, (int)b.Vb, a.dz, a.ld_dz, a.dzt, a.ld_dzt,
                      n_ht, n_dw, n_dh, a.dh, a.dW, b.acc_dh, b.acc_dW);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  trace_end(kBwdGrad, stream, 4.0 * ct * vb * H,
+            4.0 * ct * vb + 2.0 * (ct + vb) * H + 4.0 * H * (ct * (1 + b.acc_dh) + vb * (1 + b.acc_dW)));
+  return hipSuccess;
 }
 
 hipError_t launch_transpose(const uint16_t* in, int64_t ld_in, int64_t R, int64_t C, int64_t R_pad,
                             int64_t C_pad, const int32_t* tgt, int64_t V, uint16_t* out,
                             int64_t ld_out, hipStream_t stream) {
+  trace_begin(stream);
   hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)(R_pad / 64), (unsigned)(C_pad / 64)), dim3(256),
                      0, stream, in, ld_in, (int)R, (int)C, tgt, (int)V, out, ld_out);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  trace_end(kTranspose, stream, 0.0, 2.0 * (double)R * C + 2.0 * (double)R_pad * C_pad);
+  return hipSuccess;
 }
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   long long blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
+  trace_begin(stream);
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  trace_end(kFill, stream, 0.0, 4.0 * (double)n);
+  return hipSuccess;
 }
 
 }  // namespace lmh

@@ -37,10 +37,12 @@
  *    16-bit patterns (uint16_t).
  *  - Shapes: N >= 0 tokens, H > 0 hidden with H % 64 == 0, 0 < V < 2^31.
  *  - chunk_size > 0 counts flattened tokens. It bounds the backward's
- *    transient memory: the logits cotangent the backward holds at any time is
- *    at most one float32 [chunk_size, V] tensor in bytes (it is kept as bf16
- *    blocks of tokens x vocabulary). The forward holds no [tokens, vocab]
- *    transient at all. Per-token forward results do not depend on
+ *    [tokens, vocab]-shaped transient: the logits cotangent the backward
+ *    holds at any time is at most one float32 [chunk_size, V] tensor in bytes
+ *    (it is kept as two bf16 copies, token-major and vocabulary-major, of a
+ *    block of tokens x vocabulary). The backward workspace also holds bf16
+ *    transposes of W and of the hidden states (input-sized). The forward
+ *    holds no [tokens, vocab] transient at all. Per-token forward results do not depend on
  *    chunk_size; gradients depend on it only through float32 summation order.
  *  - Targets outside [0, V) (-1 included) mask the token: its logp, entropy
  *    and lse are written as 0, its dh row is written as 0 and it adds nothing
@@ -49,7 +51,8 @@
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    default stream). The library never synchronises the device, allocates
  *    no device memory and keeps no state between calls: distinct workspaces
- *    on distinct streams may be used from several threads at once.
+ *    on distinct streams may be used from several threads at once (the
+ *    optional tracing at the end of this header is the one exception).
  *  - Outputs are overwritten in full (dW is not accumulated into).
  *  - Return value: LMH_OK (0) or a negative LMH_ERR_* code. Argument checks
  *    run on the host before anything is enqueued, so a failing call enqueues
@@ -135,6 +138,29 @@ const char* lmhead_logps_last_error(void);
 
 /* Library version string. */
 const char* lmhead_logps_version(void);
+
+/*
+ * Tracing (measurement only; not needed to use the head). While enabled,
+ * every kernel launch of the library is bracketed by two HIP events on the
+ * stream it runs on and tagged with its algorithmic work. Kernel ids:
+ *   0 fwd_stats_kernel  (forward logits tiles + running statistics)
+ *   1 fwd_merge_kernel  (split merge)
+ *   2 bwd_dz_kernel     (logits recompute + cotangent block)
+ *   3 bwd_grad_kernel   (dh and dW GEMMs of one block)
+ *   4 transpose_kernel  (bf16 transposes of W and hidden)
+ *   5 fill_zero_kernel
+ * lmhead_logps_trace_enable(on) clears the totals and starts (on != 0) or
+ * stops recording. lmhead_logps_trace_read(kernel, ...) waits for the
+ * recorded launches to finish and returns, for that kernel, the launch
+ * count, the summed duration in ms and the summed algorithmic flops and
+ * bytes. This state is process-wide; enabling it adds two event records per
+ * launch. Errors: LMH_ERR_ARGS (unknown kernel id), LMH_ERR_NULL.
+ * lmhead_logps_trace_kernel_name returns NULL for an unknown id.
+ */
+int lmhead_logps_trace_enable(int on);
+int lmhead_logps_trace_read(int kernel, int64_t* launches, double* total_ms, double* flops,
+                            double* bytes);
+const char* lmhead_logps_trace_kernel_name(int kernel);
 
 #ifdef __cplusplus
 }
