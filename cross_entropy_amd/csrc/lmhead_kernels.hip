@@ -14,11 +14,12 @@
 // Every contraction runs on one MFMA tile core: a 256 x 256 output tile per
 // 512-thread workgroup (8 wave64s as 2 x 4, each owning 128 x 64),
 // v_mfma_f32_32x32x16_bf16, with both operands K-contiguous. K is staged
-// through a 4-deep ring of 32-wide LDS slices filled by direct-to-LDS loads
-// (global_load_lds_dwordx4), so three slices are in flight while one is
-// consumed and no VGPRs hold staged data. Slice rows are 64 bytes with a
+// through two 64-wide LDS slices filled by direct-to-LDS loads
+// (global_load_lds_dwordx4): the next slice lands while the current one is
+// consumed and no VGPRs hold staged data. Slice rows are 128 bytes with a
 // 16-byte-chunk XOR swizzle, which keeps the MFMA fragment reads free of
-// bank conflicts. Operands that are stored MN-contiguous (W and hidden in
+// bank conflicts. The MFMA block of each slice runs at raised wave priority
+// so the two waves sharing a SIMD keep its matrix pipe fed. Operands that are stored MN-contiguous (W and hidden in
 // the backward) are given to the core through transposed copies.
 //
 // MFMA 32x32x16 register layout used throughout (wave64): lane l supplies
@@ -39,12 +40,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 512;
 constexpr int kTile = 256;                       // output tile edge
-constexpr int kBK = 32;                          // K per LDS slice
-constexpr int kStages = 4;                       // slices in the ring
-constexpr int kRowBytes = kBK * 2;               // 64 B per staged row
+constexpr int kBK = 64;                          // K per LDS slice
+constexpr int kStages = 2;                       // slices in the ring
+constexpr int kRowBytes = kBK * 2;               // 128 B per staged row
+constexpr int kRowsPerDma = 1024 / kRowBytes;    // rows one wave-wide DMA fills
 constexpr int kOpBytes = kTile * kRowBytes;      // 16 KB per operand slice
 constexpr int kStageBytes = 2 * kOpBytes;        // A + B
 constexpr int kLdsBytes = kStages * kStageBytes; // 128 KB of the 160 KB per CU
+
+constexpr int kTPitch = kTile * 2 + 16;          // staged transposed cotangent row (bytes)
+constexpr int kDzLdsBytes = kTile * kTPitch > kLdsBytes ? kTile * kTPitch : kLdsBytes;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
@@ -92,8 +97,10 @@ struct Operand {
   int rows;
 };
 
-// 16-byte chunk index of logical chunk c of staged row r.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// XOR applied to the 16-byte chunk index of staged row r (8 chunks per row):
+// any 16 consecutive rows read at one logical chunk hit 16 distinct 16-byte
+// bank groups of the 256-byte bank line.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
@@ -114,24 +121,25 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Stage rows [0, 256) x K [k0, k0 + 32) of one operand. Each wave loads 32
-// rows as 2 x 16 rows of 4 chunks; lane l fills physical chunk l % 4 of row
-// l / 4 with the logical chunk that the swizzle puts there.
+// Stage rows [0, 256) x K [k0, k0 + 64) of one operand. Each wave loads 32
+// rows as 4 x 8 rows of 8 chunks; lane l fills physical chunk l % 8 of row
+// l / 8 with the logical chunk that the swizzle puts there.
 __device__ __forceinline__ void stage(const Operand& op, int k0, uint32_t lds_op) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = wave * 32 + q * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ swz(r);
+  for (int q = 0; q < 4; ++q) {
+    const int r0 = wave * 32 + q * kRowsPerDma;
+    const int r = r0 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
     const int rr = min(r, op.rows - 1);
     const uint16_t* g = op.base + (int64_t)rr * op.ld + k0 + c * 8;
-    dma16(g, __builtin_amdgcn_readfirstlane(lds_op + (wave * 32 + q * 16) * kRowBytes));
+    dma16(g, __builtin_amdgcn_readfirstlane(lds_op + r0 * kRowBytes));
   }
 }
 
 // The tile core: acc[i][j] (wave sub-block i of 32 A-rows, j of 32 B-rows)
-// = sum over k < K of A[row][k] * B[row][k]. K is a multiple of 32. Ends
+// = sum over k < K of A[row][k] * B[row][k]. K is a multiple of 64. Ends
 // with a barrier, so LDS may be reused as soon as it returns.
 __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int K, char* lds,
                                          f32x16 (&acc)[4][2]) {
@@ -148,35 +156,24 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
 
   const uint32_t base = lds_offset(lds);
   const int nk = K / kBK;
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) {
-    if (s < nk) {
-      stage(A, s * kBK, base + s * kStageBytes);
-      stage(B, s * kBK, base + s * kStageBytes + kOpBytes);
-    }
-  }
+  stage(A, 0, base);
+  stage(B, 0, base + kOpBytes);
   const int sw = swz(lane & 31);
   const int a_off = (wm * 128 + (lane & 31)) * kRowBytes;
   const int b_off = kOpBytes + (wn * 64 + (lane & 31)) * kRowBytes;
 
   for (int kt = 0; kt < nk; ++kt) {
-    // this wave's loads of slice kt are done once at most the later slices'
-    // 4 loads each are outstanding; the barrier then publishes everybody's
-    const int later = min(kStages - 2, nk - 1 - kt);
-    if (later >= 2) {
-      wait_vm<8>();
-    } else if (later == 1) {
-      wait_vm<4>();
-    } else {
-      wait_vm<0>();
-    }
+    // this wave's loads of slice kt are done; the barrier then publishes
+    // everybody's, and frees the other slice for the next loads
+    wait_vm<0>();
     __syncthreads();
-    if (kt + kStages - 1 < nk) {
-      const uint32_t st = base + ((kt + kStages - 1) % kStages) * kStageBytes;
-      stage(A, (kt + kStages - 1) * kBK, st);
-      stage(B, (kt + kStages - 1) * kBK, st + kOpBytes);
+    if (kt + 1 < nk) {
+      const uint32_t st = base + ((kt + 1) & 1) * kStageBytes;
+      stage(A, (kt + 1) * kBK, st);
+      stage(B, (kt + 1) * kBK, st + kOpBytes);
     }
-    const char* cur = lds + (kt % kStages) * kStageBytes;
+    const char* cur = lds + (kt & 1) * kStageBytes;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int co = (((ks * 2) + (lane >> 5)) ^ sw) * 16;
@@ -193,6 +190,7 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
   __syncthreads();
 }
@@ -378,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dz_kernel(
     const float* __restrict__ g_logp, const float* __restrict__ g_ent,
     int t0, int Ct, int v0, int Vb, int n_tt, int n_vt,
     uint16_t* __restrict__ dz, int64_t ld, uint16_t* __restrict__ dzt, int64_t ldt) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char lds[kDzLdsBytes];
   const int vid = xcd_remap(blockIdx.x, gridDim.x);
   if (vid >= n_tt * n_vt) return;
   int vt, tt;
@@ -419,12 +417,16 @@ __global__ __launch_bounds__(kThreads) void bwd_dz_kernel(
   const bool any_dead = __any(!live[0] || !live[1]);
   const bool ragged = (vw0 + 128 > Vb);
 
+  // dz goes out directly (4 consecutive vocabulary entries per lane); the
+  // vocabulary-major copy is staged transposed in LDS (rows of 256 tokens,
+  // padded to kTPitch) and streamed out as whole rows.
+  char* T = lds;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int tl = tl0 + wn * 64 + j * 32 + (lane & 31);
+    const int tc = wn * 64 + j * 32 + (lane & 31);   // tile-local token column
+    const int tl = tl0 + tc;
     const bool hit_any = __any(tr[j] >= 0 && tr[j] < 128);
     uint16_t* row = dz + (int64_t)tl * ld + vw0;
-    uint16_t* col = dzt + (int64_t)vw0 * ldt + tl;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -446,11 +448,21 @@ __global__ __launch_bounds__(kThreads) void bwd_dz_kernel(
         w.y = pack_bf16x2(v[2], v[3]);
         const int m = i * 32 + 8 * g + 4 * (lane >> 5);
         *reinterpret_cast<uint2*>(row + m) = w;
-        col[(int64_t)(m + 0) * ldt] = (uint16_t)(w.x & 0xFFFFu);
-        col[(int64_t)(m + 1) * ldt] = (uint16_t)(w.x >> 16);
-        col[(int64_t)(m + 2) * ldt] = (uint16_t)(w.y & 0xFFFFu);
-        col[(int64_t)(m + 3) * ldt] = (uint16_t)(w.y >> 16);
+        char* t = T + (wm * 128 + m) * kTPitch + tc * 2;
+        *reinterpret_cast<uint16_t*>(t) = (uint16_t)(w.x & 0xFFFFu);
+        *reinterpret_cast<uint16_t*>(t + kTPitch) = (uint16_t)(w.x >> 16);
+        *reinterpret_cast<uint16_t*>(t + 2 * kTPitch) = (uint16_t)(w.y & 0xFFFFu);
+        *reinterpret_cast<uint16_t*>(t + 3 * kTPitch) = (uint16_t)(w.y >> 16);
       }
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int p = 0; p < (kTile * kTile * 2 / 16) / kThreads; ++p) {
+    const int idx = p * kThreads + threadIdx.x;
+    const int vr = idx >> 5;          // tile-local vocabulary row
+    const int c = idx & 31;           // 16-byte chunk (8 tokens)
+    const uint4 x = *reinterpret_cast<const uint4*>(T + vr * kTPitch + c * 16);
+    *reinterpret_cast<uint4*>(dzt + (int64_t)(vl0 + vr) * ldt + tl0 + c * 8) = x;
   }
 }
 
