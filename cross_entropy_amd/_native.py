@@ -125,8 +125,8 @@ def raw_bwd(hidden, W, targets, N, H, V, chunk_size, lse, entropy, g_logp, g_ent
                                    int(workspace_bytes), stream or None)
 
 
-TRACE_KERNELS = ("fwd_stats_kernel", "fwd_merge_kernel", "bwd_dz_kernel", "bwd_grad_kernel",
-                 "transpose_kernel", "fill_zero_kernel")
+TRACE_KERNELS = ("fwd_stats_kernel", "fwd_merge_kernel", "bwd_step_kernel", "transpose_kernel",
+                 "fill_zero_kernel")
 
 
 def trace_enable(on: bool) -> None:

@@ -9,14 +9,14 @@
 //    launch fills the 256 CUs; S partial (max, exp-sum, exp-weighted sum,
 //    target logit) records per token are merged by log-sum-exp.
 //  * The backward holds the logits' cotangent as bf16 blocks of Ct tokens x
-//    Vb vocabulary entries, twice (token-major for the dh GEMM and
-//    vocabulary-major for the dW GEMM). chunk_size bounds the block: the two
-//    copies, 4 bytes per element, stay within one float32 [chunk_size, V]
-//    tensor, the transient the pages' chunked head holds per chunk. Within
-//    that bound the block shape is chosen to cut the dh / dW accumulation
-//    traffic and launch tails. The workspace also holds bf16 transposes of W
-//    and of the hidden states (input-sized), so every GEMM operand is
-//    K-contiguous.
+//    Vb vocabulary entries, double buffered so that the cotangent of the next
+//    block is formed while the gradient GEMMs of the current one run (one
+//    launch per block). chunk_size bounds the block: the two buffers, 4 bytes
+//    per element, stay within one float32 [chunk_size, V] tensor, the
+//    transient the pages' chunked head holds per chunk. Within that bound the
+//    block shape is chosen to cut the dh / dW accumulation traffic and launch
+//    count. The workspace also holds bf16 transposes of W and of the hidden
+//    states (input-sized) for the K-contiguous operands of the GEMMs.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -37,8 +37,8 @@ static int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 FwdPlan plan_forward(int64_t N, int64_t H, int64_t V) {
   (void)H;
   FwdPlan p;
-  p.n_tt = (int)ceil_div(N, kTileRows);
-  p.n_vt = (int)ceil_div(V, kTileRows);
+  p.n_tt = (int)lmh::ceil_div(N, kTileRows);
+  p.n_vt = (int)lmh::ceil_div(V, kTileRows);
   const int s_max = (int)std::min<int64_t>(p.n_vt, 128);
   // makespan in tile-steps: rounds of resident workgroups x tiles per split
   auto cost = [&](int S) {
@@ -67,18 +67,16 @@ FwdPlan plan_forward(int64_t N, int64_t H, int64_t V) {
 BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, int64_t chunk_size) {
   const int64_t T = kTileRows;
   N = std::max<int64_t>(N, 1);
-  // elements of the dz block (held as two bf16 copies, 4 bytes each): at
-  // most chunk_size * V, and at least one 256 x 256 tile.
+  // elements of one dz block (two bf16 buffers, 4 bytes per element in all):
+  // at most chunk_size * V, and at least one 256 x 256 tile.
   const double budget = std::max<double>((double)chunk_size * (double)V, (double)(T * T));
-  const int64_t n_pad = round_up(std::max<int64_t>(N, 1), T);
+  const int64_t n_pad = round_up(N, T);
   const int64_t v_pad = round_up(V, T);
-  const int64_t n_ht = ceil_div(H, T);
-  // model constants: per-CU bf16 MFMA rate at a realistic efficiency, HBM
-  // rate for the f32 accumulation traffic, per-launch cost
-  const double rate = 2.5e15 * 0.6 / kNumCUs;
+  // model: the MFMA work is fixed; what the block shape changes is the f32
+  // accumulation traffic of dh (one pass per vocabulary block) and dW (one
+  // pass per token block), and the number of launches.
   const double hbm = 5.0e12;
-  const double launch = 6e-6;
-
+  const double launch = 20e-6;
   BwdPlan best;
   double best_t = 1e300;
   for (int64_t ct = T; ct <= n_pad; ct += T) {
@@ -89,15 +87,8 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, int64_t chunk_size) {
     const int64_t n_vb = ceil_div(V, vb);
     const int64_t c2 = round_up(ceil_div(N, n_tb), T);   // even out the blocks
     const int64_t v2 = round_up(ceil_div(V, n_vb), T);
-    const double tile_dz = 2.0 * T * T * (double)H / rate;
-    const double n3 = (double)(c2 / T) * (double)(v2 / T);
-    const double t3 = std::ceil(n3 / kNumCUs) * tile_dz;
-    const double tile_dw = 2.0 * T * T * (double)c2 / rate;
-    const double tile_dh = 2.0 * T * T * (double)v2 / rate;
-    const double work45 = (double)(v2 / T) * n_ht * tile_dw + (double)(c2 / T) * n_ht * tile_dh;
-    const double t45 = work45 / kNumCUs + 0.5 * std::max(tile_dw, tile_dh);
-    const double traffic = (8.0 * N * H * n_vb + 8.0 * V * H * n_tb) / hbm * 0.3;
-    const double t = (double)(n_tb * n_vb) * (t3 + t45 + 2 * launch) + traffic;
+    const double traffic = (8.0 * N * H * n_vb + 8.0 * V * H * n_tb) / hbm;
+    const double t = (double)(n_tb * n_vb + 1) * launch + traffic;
     if (t < best_t) {
       best_t = t;
       best.Ct = c2;
@@ -110,8 +101,7 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, int64_t chunk_size) {
   best.V_pad = round_up(V, T);
   best.H_pad = round_up(H, T);
   const size_t one = (size_t)round_up(best.Ct * best.Vb * 2, 256);
-  best.dz_bytes = 2 * one;
-  best.off_dzt = one;
+  best.off_dz1 = one;
   best.off_wt = 2 * one;
   best.off_ht = best.off_wt + (size_t)round_up(best.H_pad * best.V_pad * 2, 256);
   best.bytes = best.off_ht + (size_t)round_up(best.H_pad * best.N_pad * 2, 256);
@@ -218,28 +208,68 @@ int lmhead_logps_bwd(const uint16_t* hidden, const uint16_t* W, const int32_t* t
   if (workspace_bytes < p.bytes)
     return fail(LMH_ERR_WORKSPACE, "bwd: workspace of %zu bytes, %zu needed", workspace_bytes, p.bytes);
   char* ws = static_cast<char*>(workspace);
-  lmh::BwdArgs a{hidden, W, targets, N, H, V, lse, entropy, g_logp, g_ent, dh, dW,
-                 reinterpret_cast<uint16_t*>(ws), p.Vb,
-                 reinterpret_cast<uint16_t*>(ws + p.off_dzt), p.Ct,
-                 reinterpret_cast<uint16_t*>(ws + p.off_wt), p.V_pad,
-                 reinterpret_cast<uint16_t*>(ws + p.off_ht), p.N_pad};
-  hipError_t te = lmh::launch_transpose(W, H, V, H, p.V_pad, p.H_pad, nullptr, V, a.Wt, p.V_pad, s);
+  uint16_t* dzbuf[2] = {reinterpret_cast<uint16_t*>(ws), reinterpret_cast<uint16_t*>(ws + p.off_dz1)};
+  uint16_t* Wt = reinterpret_cast<uint16_t*>(ws + p.off_wt);
+  uint16_t* ht = reinterpret_cast<uint16_t*>(ws + p.off_ht);
+  hipError_t te = lmh::launch_transpose(W, H, V, H, p.V_pad, p.H_pad, nullptr, V, Wt, p.V_pad, s);
   if (te == hipSuccess)
-    te = lmh::launch_transpose(hidden, H, N, H, p.N_pad, p.H_pad, targets, V, a.ht, p.N_pad, s);
+    te = lmh::launch_transpose(hidden, H, N, H, p.N_pad, p.H_pad, targets, V, ht, p.N_pad, s);
   if (te != hipSuccess) return fail(LMH_ERR_HIP, "bwd: launch failed: %s", hipGetErrorString(te));
-  for (int64_t tb = 0; tb < p.n_tb; ++tb) {
-    for (int64_t vb = 0; vb < p.n_vb; ++vb) {
-      lmh::BwdBlock b;
-      b.t0 = tb * p.Ct;
-      b.Ct = std::min(p.Ct, N - b.t0);
-      b.v0 = vb * p.Vb;
-      b.Vb = std::min(p.Vb, V - b.v0);
-      b.acc_dh = vb > 0;
-      b.acc_dW = tb > 0;
-      if (b.Ct <= 0 || b.Vb <= 0) continue;
-      const hipError_t e = lmh::launch_bwd_block(a, b, s);
-      if (e != hipSuccess) return fail(LMH_ERR_HIP, "bwd: launch failed: %s", hipGetErrorString(e));
+
+  lmh::BwdStep st{};
+  st.hidden = hidden;
+  st.W = W;
+  st.targets = targets;
+  st.N = (int)N;
+  st.H = (int)H;
+  st.V = (int)V;
+  st.lse = lse;
+  st.entropy = entropy;
+  st.g_logp = g_logp;
+  st.g_ent = g_ent;
+  st.ht = ht;
+  st.ld_ht = p.N_pad;
+  st.Wt = Wt;
+  st.ld_wt = p.V_pad;
+  st.dh = dh;
+  st.dW = dW;
+  st.ld_dz = p.Vb;
+  st.n_ht = (int)lmh::ceil_div(H, lmh::kTileRows);
+  // blocks in a fixed order (token blocks outer, vocabulary blocks inner);
+  // launch j forms block j's cotangent and runs block j-1's GEMMs
+  const int64_t nb = p.n_tb * p.n_vb;
+  for (int64_t j = 0; j <= nb; ++j) {
+    if (j >= 1) {
+      const int64_t g = j - 1;
+      const int64_t tb = g / p.n_vb, vb = g % p.n_vb;
+      st.g_dz = dzbuf[g & 1];
+      st.g_t0 = (int)(tb * p.Ct);
+      st.g_Ct = (int)std::min(p.Ct, N - tb * p.Ct);
+      st.g_v0 = (int)(vb * p.Vb);
+      st.g_Vb = (int)std::min(p.Vb, V - vb * p.Vb);
+      st.g_acc_dh = vb > 0;
+      st.g_acc_dW = tb > 0;
+      st.n_dw = (int)(lmh::ceil_div(st.g_Vb, lmh::kTileRows) * st.n_ht);
+      st.n_dh = (int)(lmh::ceil_div(st.g_Ct, lmh::kTileRows) * st.n_ht);
+    } else {
+      st.g_dz = nullptr;
+      st.n_dw = st.n_dh = 0;
     }
+    if (j < nb) {
+      const int64_t tb = j / p.n_vb, vb = j % p.n_vb;
+      st.z_dz = dzbuf[j & 1];
+      st.z_t0 = (int)(tb * p.Ct);
+      st.z_Ct = (int)std::min(p.Ct, N - tb * p.Ct);
+      st.z_v0 = (int)(vb * p.Vb);
+      st.z_Vb = (int)std::min(p.Vb, V - vb * p.Vb);
+      st.z_ntt = (int)lmh::ceil_div(st.z_Ct, lmh::kTileRows);
+      st.z_nvt = (int)lmh::ceil_div(st.z_Vb, lmh::kTileRows);
+    } else {
+      st.z_dz = nullptr;
+      st.z_ntt = st.z_nvt = 0;
+    }
+    const hipError_t e = lmh::launch_bwd_step(st, s);
+    if (e != hipSuccess) return fail(LMH_ERR_HIP, "bwd: launch failed: %s", hipGetErrorString(e));
   }
   return ok();
 }

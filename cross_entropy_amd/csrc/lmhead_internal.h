@@ -21,15 +21,14 @@ struct FwdPlan {
 };
 
 // Backward: the token x vocabulary plane is cut into blocks of at most
-// Ct x Vb; the block's cotangent is held twice in bf16 (dz [Ct][Vb] and
-// dzt [Vb][Ct]), i.e. 4 bytes per element like one float32 block. The
+// Ct x Vb; each block's cotangent is one bf16 buffer dz [Ct][Vb], double
+// buffered (4 bytes per element in all, like one float32 block). The
 // workspace also holds W^T [H_pad][V_pad] and hidden^T [H_pad][N_pad].
 struct BwdPlan {
   int64_t Ct = 0, Vb = 0;      // block edges (tokens, vocabulary), multiples of 256
   int64_t n_tb = 0, n_vb = 0;  // blocks along tokens and vocabulary
   int64_t N_pad = 0, V_pad = 0, H_pad = 0;
-  size_t off_dzt = 0, off_wt = 0, off_ht = 0;   // byte offsets in the workspace
-  size_t dz_bytes = 0;         // dz + dzt
+  size_t off_dz1 = 0, off_wt = 0, off_ht = 0;   // byte offsets in the workspace
   size_t bytes = 0;            // total
 };
 
@@ -49,41 +48,40 @@ struct FwdArgs {
   float* lse;
 };
 
-struct BwdArgs {
+// One backward launch: the gradient tiles of one block (n_dw + n_dh tiles,
+// none if 0) and the cotangent tiles of the next (z_ntt * z_nvt, none if 0).
+struct BwdStep {
   const uint16_t* hidden;
   const uint16_t* W;
   const int32_t* targets;
-  int64_t N, H, V;
+  int N, H, V;
   const float* lse;
   const float* entropy;
   const float* g_logp;
   const float* g_ent;
+  const uint16_t* ht;   // hidden^T [H_pad][N_pad], masked tokens zeroed
+  int64_t ld_ht;
+  const uint16_t* Wt;   // W^T [H_pad][V_pad]
+  int64_t ld_wt;
   float* dh;
   float* dW;
-  uint16_t* dz;      // [Ct][Vb] block, row stride ld_dz
-  int64_t ld_dz;
-  uint16_t* dzt;     // [Vb][Ct] block, row stride ld_dzt
-  int64_t ld_dzt;
-  uint16_t* Wt;      // W^T [H_pad][V_pad]
-  int64_t ld_wt;
-  uint16_t* ht;      // hidden^T [H_pad][N_pad], masked tokens zeroed
-  int64_t ld_ht;
-};
-
-struct BwdBlock {
-  int64_t t0, Ct;   // tokens [t0, t0 + Ct)
-  int64_t v0, Vb;   // vocabulary [v0, v0 + Vb)
-  int acc_dh;       // 0: first vocabulary block writes dh, 1: adds
-  int acc_dW;       // 0: first token block writes dW, 1: adds
+  int64_t ld_dz;        // row stride of both dz buffers
+  // gradient part
+  const uint16_t* g_dz;
+  int g_t0, g_Ct, g_v0, g_Vb, g_acc_dh, g_acc_dW;
+  int n_dw, n_dh, n_ht;
+  // cotangent part
+  uint16_t* z_dz;
+  int z_t0, z_Ct, z_v0, z_Vb, z_ntt, z_nvt;
 };
 
 // Kernel ids of the tracing facility (lmhead_trace.hip).
-enum KernelId { kFwdStats = 0, kFwdMerge, kBwdDz, kBwdGrad, kTranspose, kFill, kNumKernels };
+enum KernelId { kFwdStats = 0, kFwdMerge, kBwdStep, kTranspose, kFill, kNumKernels };
 void trace_begin(hipStream_t stream);
 void trace_end(int kernel, hipStream_t stream, double flops, double bytes);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_block(const BwdArgs& a, const BwdBlock& b, hipStream_t stream);
+hipError_t launch_bwd_step(const BwdStep& st, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_transpose(const uint16_t* in, int64_t ld_in, int64_t R, int64_t C, int64_t R_pad,
                             int64_t C_pad, const int32_t* tgt, int64_t V, uint16_t* out,

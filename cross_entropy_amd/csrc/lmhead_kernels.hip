@@ -138,9 +138,43 @@ __device__ __forceinline__ void stage(const Operand& op, int k0, uint32_t lds_op
   }
 }
 
+// Stage K-rows [k0, k0 + 64) x M [0, 256) of an MN-contiguous operand:
+// element (m, k) at base[k * ld + m]. The slice holds 64 rows of 256 m
+// (512 B each); 16-byte chunks are XOR-swizzled by 4 * (k % 4) so the
+// transposed fragment reads below hit distinct bank groups. Each wave-wide
+// DMA fills two rows.
+__device__ __forceinline__ void stage_mn(const Operand& op, int k0, uint32_t lds_op) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r0 = wave * 8 + q * 2;
+    const int r = r0 + (lane >> 5);
+    const int c = (lane & 31) ^ (4 * (r & 3));
+    const uint16_t* g = op.base + (int64_t)(k0 + r) * op.ld + c * 8;
+    dma16(g, __builtin_amdgcn_readfirstlane(lds_op + r0 * (kTile * 2)));
+  }
+}
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v* lds_s4;
+
+// LDS transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane j
+// receives element (j & 3) of the 8-byte reads of lanes (j >> 2) + 4q,
+// q = 0..3. Pointing lane s of the group at row k + (s >> 2), columns
+// m + 4 (s & 3) .. +3 therefore hands lane j the 4 consecutive K values
+// (k .. k+3) of column m + j.
+__device__ __forceinline__ short4v ds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s4)(const __attribute__((address_space(3))) char*)p);
+}
+
 // The tile core: acc[i][j] (wave sub-block i of 32 A-rows, j of 32 B-rows)
-// = sum over k < K of A[row][k] * B[row][k]. K is a multiple of 64. Ends
-// with a barrier, so LDS may be reused as soon as it returns.
+// = sum over k < K of A[row][k] * B[row][k]. K is a multiple of 64. With
+// A_MN the A operand is MN-contiguous (see stage_mn) and its fragments are
+// assembled with transposed LDS reads. Ends with a barrier, so LDS may be
+// reused as soon as it returns.
+template <bool A_MN>
 __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int K, char* lds,
                                          f32x16 (&acc)[4][2]) {
   const int lane = threadIdx.x & 63;
@@ -156,11 +190,18 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
 
   const uint32_t base = lds_offset(lds);
   const int nk = K / kBK;
-  stage(A, 0, base);
+  if (A_MN) stage_mn(A, 0, base); else stage(A, 0, base);
   stage(B, 0, base + kOpBytes);
   const int sw = swz(lane & 31);
   const int a_off = (wm * 128 + (lane & 31)) * kRowBytes;
   const int b_off = kOpBytes + (wn * 64 + (lane & 31)) * kRowBytes;
+  // transposed A reads: lane group gq = lane / 16 covers columns
+  // 16 * (gq & 1) .. +15 of a 32-column sub-block and K rows 8 * (gq >> 1) ..
+  const int gq = lane >> 4;
+  const int sl = lane & 15;
+  const int t_row = 8 * (gq >> 1) + (sl >> 2);             // + 16 ks (+ 4 for the upper half)
+  const int t_chunk = wm * 16 + 2 * (gq & 1) + ((sl & 3) >> 1);   // + 4 i, before the swizzle
+  const int t_byte = 8 * (sl & 1);
 
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's loads of slice kt are done; the barrier then publishes
@@ -169,7 +210,7 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
     __syncthreads();
     if (kt + 1 < nk) {
       const uint32_t st = base + ((kt + 1) & 1) * kStageBytes;
-      stage(A, (kt + 1) * kBK, st);
+      if (A_MN) stage_mn(A, (kt + 1) * kBK, st); else stage(A, (kt + 1) * kBK, st);
       stage(B, (kt + 1) * kBK, st + kOpBytes);
     }
     const char* cur = lds + (kt & 1) * kStageBytes;
@@ -178,9 +219,22 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int co = (((ks * 2) + (lane >> 5)) ^ sw) * 16;
       bf16x8 a[4], b[2];
+      if (A_MN) {
+        const int row = ks * 16 + t_row;          // row & 3 == (row + 4) & 3
+        const int x = row & 3;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(cur + a_off + i * 32 * kRowBytes + co);
+        for (int i = 0; i < 4; ++i) {
+          const char* p = cur + row * (kTile * 2) + ((t_chunk | ((i ^ x) << 2)) << 4) + t_byte;
+          const short4v lo = ds_read_tr(p);
+          const short4v hi = ds_read_tr(p + 4 * (kTile * 2));
+          const short4v v8[2] = {lo, hi};
+          a[i] = __builtin_bit_cast(bf16x8, v8);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a[i] = *reinterpret_cast<const bf16x8*>(cur + a_off + i * 32 * kRowBytes + co);
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         b[j] = *reinterpret_cast<const bf16x8*>(cur + b_off + j * 32 * kRowBytes + co);
@@ -257,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
     const int v0 = vt * kTile;
     const Operand oa{W + (int64_t)v0 * H, H, min(kTile, V - v0)};
     f32x16 acc[4][2];
-    mma_tile(oa, ob, H, lds, acc);
+    mma_tile<false>(oa, ob, H, lds, acc);
 
     const int vrow0 = v0 + wm * 128;
     if (vrow0 + 128 > V) {   // ragged last tile: rows past V take no part
@@ -361,37 +415,34 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Backward, step 1: recompute a logits tile of the block [t0, t0+Ct) x
-// [v0, v0+Vb) and write its cotangent
+// Backward. The token x vocabulary plane is cut into blocks; each block's
+// cotangent is held as one bf16 buffer dz[token - t0][vocab - v0] and read
+// by both gradient GEMMs (the dW GEMM through transposed LDS reads). Launch
+// j of the backward carries the dh / dW tiles of block j - 1 (reading dz
+// buffer (j - 1) % 2) and the cotangent tiles of block j (writing buffer
+// j % 2): the short cotangent tiles fill the tail of the long GEMM tiles,
+// and stream order makes every buffer's writes precede its reads.
+
+// Cotangent tile: recompute a 256 x 256 logits tile of block
+// [t0, t0 + Ct) x [v0, v0 + Vb) and write
 //   dz = g_l (onehot - p) - g_e p (log p + entropy),  p = 2^(z log2e - lse log2e)
-// as bf16 twice: dz[token - t0][vocab - v0] (row stride ld) for the dh GEMM
-// and dzt[vocab - v0][token - t0] (row stride ldt) for the dW GEMM, so both
-// read a K-contiguous operand. Rows/columns outside the block, masked tokens
-// and vocabulary past V are written as 0, so the gradient GEMMs can run over
-// the padded block.
-__global__ __launch_bounds__(kThreads) void bwd_dz_kernel(
-    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W,
-    const int32_t* __restrict__ targets, int V, int H,
-    const float* __restrict__ lse, const float* __restrict__ entropy,
-    const float* __restrict__ g_logp, const float* __restrict__ g_ent,
-    int t0, int Ct, int v0, int Vb, int n_tt, int n_vt,
-    uint16_t* __restrict__ dz, int64_t ld, uint16_t* __restrict__ dzt, int64_t ldt) {
-  __shared__ __attribute__((aligned(16))) char lds[kDzLdsBytes];
-  const int vid = xcd_remap(blockIdx.x, gridDim.x);
-  if (vid >= n_tt * n_vt) return;
+// as bf16. Tokens past the block, masked tokens and vocabulary past the block
+// are written as 0, so the gradient GEMMs can run over the padded block.
+__device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
   int vt, tt;
-  raster(vid, n_vt, n_tt, 4, vt, tt);
+  raster(vid, s.z_nvt, s.z_ntt, 4, vt, tt);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1;
   const int wn = wave >> 1;
+  const int t0 = s.z_t0, Ct = s.z_Ct, v0 = s.z_v0, Vb = s.z_Vb, H = s.H, V = s.V;
   const int tl0 = tt * kTile;   // token offset in the block
   const int vl0 = vt * kTile;   // vocabulary offset in the block
 
-  const Operand oa{W + (int64_t)(v0 + vl0) * H, H, min(kTile, Vb - vl0)};
-  const Operand ob{hidden + (int64_t)(t0 + tl0) * H, H, min(kTile, Ct - tl0)};
+  const Operand oa{s.W + (int64_t)(v0 + vl0) * H, H, min(kTile, Vb - vl0)};
+  const Operand ob{s.hidden + (int64_t)(t0 + tl0) * H, H, min(kTile, Ct - tl0)};
   f32x16 acc[4][2];
-  mma_tile(oa, ob, H, lds, acc);
+  mma_tile<false>(oa, ob, H, lds, acc);
 
   float nlseL[2], c0[2], c1[2], gl[2];
   int tr[2];
@@ -402,12 +453,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dz_kernel(
     const int tl = tl0 + wn * 64 + j * 32 + (lane & 31);
     const int tok = t0 + tl;
     int t = -1;
-    if (tl < Ct) t = targets[tok];
+    if (tl < Ct) t = s.targets[tok];
     live[j] = (t >= 0) && (t < V);
-    const float L = live[j] ? lse[tok] : 0.0f;
-    const float Hn = (live[j] && entropy != nullptr) ? entropy[tok] : 0.0f;
-    const float ga = (live[j] && g_logp != nullptr) ? g_logp[tok] : 0.0f;
-    const float gb = (live[j] && g_ent != nullptr) ? g_ent[tok] : 0.0f;
+    const float L = live[j] ? s.lse[tok] : 0.0f;
+    const float Hn = (live[j] && s.entropy != nullptr) ? s.entropy[tok] : 0.0f;
+    const float ga = (live[j] && s.g_logp != nullptr) ? s.g_logp[tok] : 0.0f;
+    const float gb = (live[j] && s.g_ent != nullptr) ? s.g_ent[tok] : 0.0f;
     nlseL[j] = -L * kLog2e;
     c0[j] = -(ga + gb * Hn);     // dz = p * (c1 * d + c0) (+ g_l at the target), d = log2 p
     c1[j] = -(gb * kLn2);
@@ -417,16 +468,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dz_kernel(
   const bool any_dead = __any(!live[0] || !live[1]);
   const bool ragged = (vw0 + 128 > Vb);
 
-  // dz goes out directly (4 consecutive vocabulary entries per lane); the
-  // vocabulary-major copy is staged transposed in LDS (rows of 256 tokens,
-  // padded to kTPitch) and streamed out as whole rows.
-  char* T = lds;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int tc = wn * 64 + j * 32 + (lane & 31);   // tile-local token column
-    const int tl = tl0 + tc;
+    const int tl = tl0 + wn * 64 + j * 32 + (lane & 31);
     const bool hit_any = __any(tr[j] >= 0 && tr[j] < 128);
-    uint16_t* row = dz + (int64_t)tl * ld + vw0;
+    uint16_t* row = s.z_dz + (int64_t)tl * s.ld_dz + vw0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -446,99 +492,104 @@ __global__ __launch_bounds__(kThreads) void bwd_dz_kernel(
         uint2 w;
         w.x = pack_bf16x2(v[0], v[1]);
         w.y = pack_bf16x2(v[2], v[3]);
-        const int m = i * 32 + 8 * g + 4 * (lane >> 5);
-        *reinterpret_cast<uint2*>(row + m) = w;
-        char* t = T + (wm * 128 + m) * kTPitch + tc * 2;
-        *reinterpret_cast<uint16_t*>(t) = (uint16_t)(w.x & 0xFFFFu);
-        *reinterpret_cast<uint16_t*>(t + kTPitch) = (uint16_t)(w.x >> 16);
-        *reinterpret_cast<uint16_t*>(t + 2 * kTPitch) = (uint16_t)(w.y & 0xFFFFu);
-        *reinterpret_cast<uint16_t*>(t + 3 * kTPitch) = (uint16_t)(w.y >> 16);
+        *reinterpret_cast<uint2*>(row + i * 32 + 8 * g + 4 * (lane >> 5)) = w;
       }
-  }
-  __syncthreads();
-#pragma unroll 4
-  for (int p = 0; p < (kTile * kTile * 2 / 16) / kThreads; ++p) {
-    const int idx = p * kThreads + threadIdx.x;
-    const int vr = idx >> 5;          // tile-local vocabulary row
-    const int c = idx & 31;           // 16-byte chunk (8 tokens)
-    const uint4 x = *reinterpret_cast<const uint4*>(T + vr * kTPitch + c * 16);
-    *reinterpret_cast<uint4*>(dzt + (int64_t)(vl0 + vr) * ldt + tl0 + c * 8) = x;
   }
 }
 
-// ---------------------------------------------------------------------------
-// Backward, step 2: both gradient GEMMs of one block in one launch, all
-// operands K-contiguous.
-//   dW tiles (first, the longer ones): dW[v0 + m][n] (+)= sum_k dzt[m][k] ht[n][t0 + k]
-//   dh tiles: dh[t0 + m][n] (+)= sum_k dz[m][k] Wt[n][v0 + k]
-// ht = hidden^T with masked tokens zeroed, Wt = W^T. `acc_dW` / `acc_dh`
-// select accumulate-into (later blocks) or overwrite (first block of the
-// fixed block order), which keeps the sums deterministic.
-__global__ __launch_bounds__(kThreads) void bwd_grad_kernel(
-    const uint16_t* __restrict__ ht, int64_t ld_ht, const uint16_t* __restrict__ Wt, int64_t ld_wt,
-    const int32_t* __restrict__ targets, int H, int V, int t0, int Ct, int v0, int Vb,
-    const uint16_t* __restrict__ dz, int64_t ld, const uint16_t* __restrict__ dzt, int64_t ldt,
-    int n_ht, int n_dw, int n_dh, float* __restrict__ dh, float* __restrict__ dW, int acc_dh,
-    int acc_dW) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  const int vid = xcd_remap(blockIdx.x, gridDim.x);
-  if (vid >= n_dw + n_dh) return;
+// dW tile: dW[v0 + m][n] (+)= sum_k dz[k][m] ht[n][t0 + k] over the block's
+// tokens (A = dz read MN-contiguous, B = hidden^T with masked tokens zeroed).
+__device__ __forceinline__ void dw_tile(const BwdStep& s, int vid, char* lds) {
+  int mt, hb;
+  raster(vid, s.n_dw / s.n_ht, s.n_ht, 4, mt, hb);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1;
   const int wn = wave >> 1;
+  const int m0 = mt * kTile;
+  const int h0 = hb * kTile;
+  const int H = s.H;
+  const Operand oa{s.g_dz + m0, s.ld_dz, kTile};
+  const Operand ob{s.ht + (int64_t)h0 * s.ld_ht + s.g_t0, s.ld_ht, kTile};
   f32x16 acc[4][2];
+  mma_tile<true>(oa, ob, (s.g_Ct + kBK - 1) / kBK * kBK, lds, acc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * 128 + acc_row(i, r, lane);
+      if (m >= s.g_Vb) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = h0 + wn * 64 + j * 32 + (lane & 31);
+        if (n < H) {
+          float* p = s.dW + (int64_t)(s.g_v0 + m) * H + n;
+          *p = s.g_acc_dW ? (*p + acc[i][j][r]) : acc[i][j][r];
+        }
+      }
+    }
+}
 
-  if (vid < n_dw) {
-    int mt, hb;
-    raster(vid, n_dw / n_ht, n_ht, 4, mt, hb);
-    const int m0 = mt * kTile;
-    const int h0 = hb * kTile;
-    const Operand oa{dzt + (int64_t)m0 * ldt, ldt, kTile};
-    const Operand ob{ht + (int64_t)h0 * ld_ht + t0, ld_ht, kTile};
-    mma_tile(oa, ob, (Ct + kBK - 1) / kBK * kBK, lds, acc);
+// dh tile: dh[t0 + m][n] (+)= sum_k dz[m][k] Wt[n][v0 + k] over the block's
+// vocabulary; masked token rows are written as 0.
+__device__ __forceinline__ void dh_tile(const BwdStep& s, int vid, char* lds) {
+  int mt, hb;
+  raster(vid, s.n_dh / s.n_ht, s.n_ht, 4, mt, hb);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+  const int m0 = mt * kTile;
+  const int h0 = hb * kTile;
+  const int H = s.H, V = s.V;
+  const Operand oa{s.g_dz + (int64_t)m0 * s.ld_dz, s.ld_dz, kTile};
+  const Operand ob{s.Wt + (int64_t)h0 * s.ld_wt + s.g_v0, s.ld_wt, kTile};
+  f32x16 acc[4][2];
+  mma_tile<false>(oa, ob, (s.g_Vb + kBK - 1) / kBK * kBK, lds, acc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 128 + acc_row(i, r, lane);
-        if (m >= Vb) continue;
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * 128 + acc_row(i, r, lane);
+      if (m >= s.g_Ct) continue;
+      const int tok = s.g_t0 + m;
+      const int t = s.targets[tok];
+      const bool live = (t >= 0) && (t < V);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = h0 + wn * 64 + j * 32 + (lane & 31);
-          if (n < H) {
-            float* p = dW + (int64_t)(v0 + m) * H + n;
-            *p = acc_dW ? (*p + acc[i][j][r]) : acc[i][j][r];
-          }
+      for (int j = 0; j < 2; ++j) {
+        const int n = h0 + wn * 64 + j * 32 + (lane & 31);
+        if (n < H) {
+          float* p = s.dh + (int64_t)tok * H + n;
+          const float v = live ? acc[i][j][r] : 0.0f;
+          *p = s.g_acc_dh ? (*p + v) : v;
         }
       }
-  } else {
-    int mt, hb;
-    raster(vid - n_dw, n_dh / n_ht, n_ht, 4, mt, hb);
-    const int m0 = mt * kTile;
-    const int h0 = hb * kTile;
-    const Operand oa{dz + (int64_t)m0 * ld, ld, kTile};
-    const Operand ob{Wt + (int64_t)h0 * ld_wt + v0, ld_wt, kTile};
-    mma_tile(oa, ob, (Vb + kBK - 1) / kBK * kBK, lds, acc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 128 + acc_row(i, r, lane);
-        if (m >= Ct) continue;
-        const int tok = t0 + m;
-        const int t = targets[tok];
-        const bool live = (t >= 0) && (t < V);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = h0 + wn * 64 + j * 32 + (lane & 31);
-          if (n < H) {
-            float* p = dh + (int64_t)tok * H + n;
-            const float v = live ? acc[i][j][r] : 0.0f;
-            *p = acc_dh ? (*p + v) : v;
-          }
-        }
-      }
+    }
+}
+
+// One backward launch: each XCD (workgroups are dealt to the 8 XCDs
+// round-robin) takes an equal share of the gradient tiles, then an equal
+// share of the cotangent tiles, so the long tiles start first everywhere and
+// the short ones fill the tail.
+__global__ __launch_bounds__(kThreads) void bwd_step_kernel(const BwdStep s) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const int xcd = blockIdx.x & 7;
+  const int loc = blockIdx.x >> 3;
+  const int n_g = s.n_dw + s.n_dh;
+  const int n_z = s.z_ntt * s.z_nvt;
+  const int g_lo = xcd * n_g / 8;
+  const int g_cnt = (xcd + 1) * n_g / 8 - g_lo;
+  const int z_lo = xcd * n_z / 8;
+  const int z_cnt = (xcd + 1) * n_z / 8 - z_lo;
+  if (loc < g_cnt) {
+    const int g = g_lo + loc;
+    if (g < s.n_dw) {
+      dw_tile(s, g, lds);
+    } else {
+      dh_tile(s, g - s.n_dw, lds);
+    }
+  } else if (loc - g_cnt < z_cnt) {
+    dz_tile(s, z_lo + loc - g_cnt, lds);
   }
 }
 
@@ -623,30 +674,27 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   return hipSuccess;
 }
 
-hipError_t launch_bwd_block(const BwdArgs& a, const BwdBlock& b, hipStream_t stream) {
-  const int n_tt = (int)((b.Ct + kTile - 1) / kTile);
-  const int n_vt = (int)((b.Vb + kTile - 1) / kTile);
-  const double ct = (double)b.Ct, vb = (double)b.Vb, H = (double)a.H;
+hipError_t launch_bwd_step(const BwdStep& st, hipStream_t stream) {
+  const int n_g = st.n_dw + st.n_dh;
+  const int n_z = st.z_ntt * st.z_nvt;
+  int per = 0;
+  for (int x = 0; x < 8; ++x)
+    per = max(per, ((x + 1) * n_g / 8 - x * n_g / 8) + ((x + 1) * n_z / 8 - x * n_z / 8));
+  if (per == 0) return hipSuccess;
+  const double H = (double)st.H;
+  const double gc = (double)st.g_Ct, gv = (double)st.g_Vb;
+  const double zc = (double)st.z_Ct, zv = (double)st.z_Vb;
   trace_begin(stream);
-  hipLaunchKernelGGL(bwd_dz_kernel, dim3(round8((long long)n_tt * n_vt)), dim3(kThreads), 0, stream,
-                     a.hidden, a.W, a.targets, (int)a.V, (int)a.H, a.lse, a.entropy, a.g_logp,
-                     a.g_ent, (int)b.t0, (int)b.Ct, (int)b.v0, (int)b.Vb, n_tt, n_vt, a.dz, a.ld_dz,
-                     a.dzt, a.ld_dzt);
-  hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL(bwd_step_kernel, dim3(8 * per), dim3(kThreads), 0, stream, st);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  trace_end(kBwdDz, stream, 2.0 * ct * vb * H, 2.0 * (ct + vb) * H + 4.0 * ct * vb + 20.0 * ct);
-  trace_begin(stream);
-  const int n_ht = (int)((a.H + kTile - 1) / kTile);
-  const int n_dw = n_vt * n_ht;
-  const int n_dh = n_tt * n_ht;
-  hipLaunchKernelGGL(bwd_grad_kernel, dim3(round8((long long)n_dw + n_dh)), dim3(kThreads), 0,
-                     stream, a.ht, a.ld_ht, a.Wt, a.ld_wt, a.targets, (int)a.H, (int)a.V,
-                     (int)b.t0, (int)b.Ct, (int)b.v0, (int)b.Vb, a.dz, a.ld_dz, a.dzt, a.ld_dzt,
-                     n_ht, n_dw, n_dh, a.dh, a.dW, b.acc_dh, b.acc_dW);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  trace_end(kBwdGrad, stream, 4.0 * ct * vb * H,
-            4.0 * ct * vb + 2.0 * (ct + vb) * H + 4.0 * H * (ct * (1 + b.acc_dh) + vb * (1 + b.acc_dW)));
+  // algorithmic work: 2 Ct Vb H per GEMM (dh, dW, and the recomputed logits);
+  // bytes: the dz block written once and read once, operand panels, f32 outputs
+  const double fl = (n_g ? 4.0 * gc * gv * H : 0.0) + (n_z ? 2.0 * zc * zv * H : 0.0);
+  const double by = (n_g ? 2.0 * gc * gv + 2.0 * (gc + gv) * H +
+                               4.0 * H * (gc * (1 + st.g_acc_dh) + gv * (1 + st.g_acc_dW)) : 0.0) +
+                    (n_z ? 2.0 * zc * zv + 2.0 * (zc + zv) * H + 20.0 * zc : 0.0);
+  trace_end(kBwdStep, stream, fl, by);
   return hipSuccess;
 }
 

@@ -38,8 +38,7 @@ Totals g_totals[kNumKernels];
 thread_local hipEvent_t t_start = nullptr;
 
 const char* const kNames[kNumKernels] = {
-    "fwd_stats_kernel", "fwd_merge_kernel", "bwd_dz_kernel",
-    "bwd_grad_kernel",  "transpose_kernel", "fill_zero_kernel",
+    "fwd_stats_kernel", "fwd_merge_kernel", "bwd_step_kernel", "transpose_kernel", "fill_zero_kernel",
 };
 
 hipEvent_t take_event() {

@@ -39,8 +39,9 @@
  *  - chunk_size > 0 counts flattened tokens. It bounds the backward's
  *    [tokens, vocab]-shaped transient: the logits cotangent the backward
  *    holds at any time is at most one float32 [chunk_size, V] tensor in bytes
- *    (it is kept as two bf16 copies, token-major and vocabulary-major, of a
- *    block of tokens x vocabulary). The backward workspace also holds bf16
+ *    (it is kept as two bf16 buffers of a block of tokens x vocabulary, the
+ *    next block's formed while the current one's is used). The backward
+ *    workspace also holds bf16
  *    transposes of W and of the hidden states (input-sized). The forward
  *    holds no [tokens, vocab] transient at all. Per-token forward results do not depend on
  *    chunk_size; gradients depend on it only through float32 summation order.
@@ -145,10 +146,10 @@ const char* lmhead_logps_version(void);
  * stream it runs on and tagged with its algorithmic work. Kernel ids:
  *   0 fwd_stats_kernel  (forward logits tiles + running statistics)
  *   1 fwd_merge_kernel  (split merge)
- *   2 bwd_dz_kernel     (logits recompute + cotangent block)
- *   3 bwd_grad_kernel   (dh and dW GEMMs of one block)
- *   4 transpose_kernel  (bf16 transposes of W and hidden)
- *   5 fill_zero_kernel
+ *   2 bwd_step_kernel   (dh and dW GEMMs of one block + the logits recompute
+ *                        and cotangent of the next block)
+ *   3 transpose_kernel  (bf16 transposes of W and hidden)
+ *   4 fill_zero_kernel
  * lmhead_logps_trace_enable(on) clears the totals and starts (on != 0) or
  * stops recording. lmhead_logps_trace_read(kernel, ...) waits for the
  * recorded launches to finish and returns, for that kernel, the launch
