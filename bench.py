@@ -71,7 +71,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--cpu-sample", type=int, default=192, help="tokens the CPU oracle runs on")
+    ap.add_argument("--cpu-sample", type=int, default=64, help="tokens the CPU oracle runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -1,0 +1,167 @@
+"""Properties of the HIP path that hold at any size, through the C ABI:
+determinism, chunk-size (in)variance, masking with non-finite hidden rows,
+the optional entropy, the log-prob-only backward, empty inputs, streams."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle.lmhead_oracle as O
+from gpu_common import assert_grad_close, assert_stats_close, dev, dev_bits, log, run_head
+from synthetic import f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _case(seed, N, H, V, w_std=0.05, n_masked=0):
+    rng = np.random.default_rng(seed)
+    h = f32_to_bf16_bits(rng.standard_normal((N, H)).astype(np.float32))
+    W = f32_to_bf16_bits((rng.standard_normal((V, H)) * w_std).astype(np.float32))
+    t = rng.integers(0, V, size=N).astype(np.int32)
+    if n_masked:
+        t[rng.choice(N, size=n_masked, replace=False)] = -1
+    g_l = rng.standard_normal(N).astype(np.float32)
+    g_e = (rng.standard_normal(N) * 0.1).astype(np.float32)
+    return h, W, t, g_l, g_e
+
+
+def test_bitwise_deterministic():
+    """Two runs give identical bits: fixed reduction orders, no atomics."""
+    h, W, t, g_l, g_e = _case(1, 1100, 256, 5000, n_masked=30)
+    log("[props] determinism")
+    a = run_head(h, W, t, 64, g_l, g_e)
+    b = run_head(h, W, t, 64, g_l, g_e)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_chunk_size_changes_only_gradient_summation_order():
+    """Per-token forward values are bitwise independent of chunk_size (the
+    forward has no chunk-shaped transient); gradients differ only by float32
+    summation order (google/tunix #2876: chunk 4096 vs 1024 within f32
+    summation order)."""
+    f = json.load(open(os.path.join(GOLDEN, "pages_figures.json")))["chunk_4096_vs_1024_numerics"]
+    h, W, t, g_l, g_e = _case(2, 1500, 256, 6000, n_masked=20)
+    log("[props] chunk sizes")
+    runs = {C: run_head(h, W, t, C, g_l, g_e) for C in (1, 37, 256, 1024, 4096)}
+    ref = runs[4096]
+    for C, r in runs.items():
+        for k in ("logp", "entropy", "lse"):
+            assert np.array_equal(r[k], ref[k]), (C, k)
+        for k in ("dh", "dW"):
+            scale = np.abs(ref[k]).max()
+            diff = np.abs(r[k] - ref[k]).max()
+            # pages' figure: 6.5e-5 on a gradient of max 83 (7.8e-7 relative)
+            assert diff <= max(50 * f["max_abs_diff_grad"] / f["grad_max_abs"], 1e-5) * scale, (C, k, diff / scale)
+
+
+def test_nonfinite_hidden_at_masked_positions_changes_nothing():
+    """NaN / +-inf hidden rows at masked positions leave every output bit
+    unchanged (tunix #2913 tests non-finite hidden states at masked
+    positions)."""
+    h, W, t, g_l, g_e = _case(3, 600, 128, 2000)
+    t[[5, 77, 300, 599]] = [-1, 2000, -9, -1]
+    log("[props] non-finite masked hidden")
+    a = run_head(h, W, t, 100, g_l, g_e)
+    h2 = h.copy()
+    h2[5] = 0x7FC0       # NaN
+    h2[77] = 0x7F80      # +inf
+    h2[300, ::2] = 0xFF80  # -inf
+    h2[599] = 0x7FC1
+    b = run_head(h2, W, t, 100, g_l, g_e)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    for k in ("logp", "entropy", "lse"):
+        assert np.all(a[k][[5, 77, 300, 599]] == 0.0)
+    assert np.all(a["dh"][[5, 77, 300, 599]] == 0.0)
+    assert np.all(np.isfinite(a["dW"]))
+
+
+def test_entropy_optional_and_logprob_only_backward():
+    """Forward without entropy gives the same logp / lse; the backward with
+    only a log-prob cotangent (GRPO case: no entropy, no g_ent) matches the
+    oracle with g_ent = 0."""
+    h, W, t, g_l, _ = _case(4, 700, 192, 3001, n_masked=11)
+    log("[props] entropy optional / GRPO backward")
+    full = run_head(h, W, t, 128, g_l, None, with_entropy=True, backward=False)
+    part = run_head(h, W, t, 128, g_l, None, with_entropy=False, backward=True, entropy_grad=False)
+    assert part["entropy"] is None
+    assert np.array_equal(full["logp"], part["logp"]) and np.array_equal(full["lse"], part["lse"])
+    ref = O.forward_backward(h, W, t, 128, g_l, None)
+    valid = t >= 0
+    assert_stats_close(part["logp"][valid], ref["logp"][valid], "logp")
+    assert_grad_close(part["dh"], ref["dh"], "dh (logp cotangent only)")
+    assert_grad_close(part["dW"], ref["dW"], "dW (logp cotangent only)")
+
+
+def test_entropy_cotangent_only_backward():
+    """g_logp absent (zeros) and only an entropy cotangent: the entropy term
+    of dz alone."""
+    h, W, t, _, g_e = _case(5, 400, 128, 1500, n_masked=4)
+    g_e = g_e * 10
+    log("[props] entropy-only backward")
+    import cross_entropy_amd as lm
+    hd, Wd, td = dev_bits(h), dev_bits(W), dev(t)
+    logp, ent, lse = lm.forward(hd, Wd, td, 64)
+    dh, dW = lm.backward(hd, Wd, td, 64, lse, ent, None, dev(g_e))
+    ref = O.forward_backward(h, W, t, 64, None, g_e)
+    assert_grad_close(dh.cpu().numpy(), ref["dh"], "dh (entropy cotangent only)")
+    assert_grad_close(dW.cpu().numpy(), ref["dW"], "dW (entropy cotangent only)")
+
+
+def test_empty_and_all_masked():
+    import torch
+    import cross_entropy_amd as lm
+    log("[props] empty and all-masked")
+    H, V = 128, 700
+    W_bits = f32_to_bf16_bits(np.random.default_rng(6).standard_normal((V, H)).astype(np.float32))
+    W = dev_bits(W_bits)
+    h0 = torch.zeros((0, H), dtype=torch.int16, device="cuda")
+    t0 = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    logp, ent, lse = lm.forward(h0, W, t0, 16)
+    assert logp.numel() == 0
+    dh, dW = lm.backward(h0, W, t0, 16, lse, ent, logp, ent)
+    torch.cuda.synchronize()
+    assert dW.shape == (V, H) and bool((dW == 0).all())
+    # every token masked: all outputs zero, dW zero
+    h, _, _, g_l, g_e = _case(7, 300, H, V)
+    t = np.full(300, -1, dtype=np.int32)
+    t[::2] = V + 5
+    r = run_head(h, W_bits, t, 50, g_l, g_e)
+    for k in r:
+        assert np.all(r[k] == 0.0), k
+
+
+def test_runs_on_a_non_default_stream_and_reuses_one_workspace():
+    import torch
+    import cross_entropy_amd as lm
+    h, W, t, g_l, g_e = _case(8, 520, 256, 2100, n_masked=7)
+    log("[props] side stream + shared workspace")
+    ref = run_head(h, W, t, 64, g_l, g_e)
+    hd, Wd, td, gl, ge = dev_bits(h), dev_bits(W), dev(t), dev(g_l), dev(g_e)
+    ws = lm.workspace_for(hd, Wd, 64, with_backward=True)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        logp, ent, lse = lm.forward(hd, Wd, td, 64, workspace=ws, stream=side)
+        dh, dW = lm.backward(hd, Wd, td, 64, lse, ent, gl, ge, workspace=ws, stream=side)
+    side.synchronize()
+    for k, v in (("logp", logp), ("entropy", ent), ("lse", lse), ("dh", dh), ("dW", dW)):
+        assert np.array_equal(v.cpu().numpy(), ref[k]), k
+
+
+def test_tracing_counts_launches():
+    import cross_entropy_amd as lm
+    from cross_entropy_amd import _native
+    h, W, t, g_l, g_e = _case(9, 300, 128, 1000)
+    _native.trace_enable(True)
+    run_head(h, W, t, 32, g_l, g_e)
+    tr = _native.trace_read()
+    _native.trace_enable(False)
+    assert tr["fwd_stats_kernel"]["launches"] == 1 and tr["fwd_merge_kernel"]["launches"] == 1
+    assert tr["bwd_step_kernel"]["launches"] >= 2 and tr["transpose_kernel"]["launches"] == 2
+    assert abs(tr["fwd_stats_kernel"]["flops"] - 2.0 * 300 * 128 * 1000) < 1.0
+    assert tr["fwd_stats_kernel"]["ms"] > 0.0
+    _ = lm
