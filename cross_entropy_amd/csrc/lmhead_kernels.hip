@@ -174,6 +174,14 @@ __device__ __forceinline__ short4v ds_read_tr(const char* p) {
 // A_MN the A operand is MN-contiguous (see stage_mn) and its fragments are
 // assembled with transposed LDS reads. Ends with a barrier, so LDS may be
 // reused as soon as it returns.
+//
+// Schedule of one 64-deep slice k (4 steps of 16): the fragments of step
+// s + 1 are read into the other register set while the 8 MFMAs of step s
+// run; the loads of slice k + 1 are issued during steps 0 (A) and 1 (B);
+// the barrier that publishes slice k + 1 sits halfway through the MFMAs of
+// the last step, and the first fragments of slice k + 1 are read right
+// after it, behind the remaining MFMAs, so the matrix pipe never restarts
+// from an empty register set.
 template <bool A_MN>
 __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int K, char* lds,
                                          f32x16 (&acc)[4][2]) {
@@ -190,8 +198,6 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
 
   const uint32_t base = lds_offset(lds);
   const int nk = K / kBK;
-  if (A_MN) stage_mn(A, 0, base); else stage(A, 0, base);
-  stage(B, 0, base + kOpBytes);
   const int sw = swz(lane & 31);
   const int a_off = (wm * 128 + (lane & 31)) * kRowBytes;
   const int b_off = kOpBytes + (wn * 64 + (lane & 31)) * kRowBytes;
@@ -203,47 +209,73 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
   const int t_chunk = wm * 16 + 2 * (gq & 1) + ((sl & 3) >> 1);   // + 4 i, before the swizzle
   const int t_byte = 8 * (sl & 1);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // this wave's loads of slice kt are done; the barrier then publishes
-    // everybody's, and frees the other slice for the next loads
-    wait_vm<0>();
-    __syncthreads();
-    if (kt + 1 < nk) {
-      const uint32_t st = base + ((kt + 1) & 1) * kStageBytes;
-      if (A_MN) stage_mn(A, (kt + 1) * kBK, st); else stage(A, (kt + 1) * kBK, st);
-      stage(B, (kt + 1) * kBK, st + kOpBytes);
-    }
-    const char* cur = lds + (kt & 1) * kStageBytes;
-    __builtin_amdgcn_s_setprio(1);
+  bf16x8 fa[2][4], fb[2][2];
+  auto read_frags = [&](int slice, int ks, int buf) {
+    const char* cur = lds + (slice & 1) * kStageBytes;
+    const int co = (((ks * 2) + (lane >> 5)) ^ sw) * 16;
+    if (A_MN) {
+      const int row = ks * 16 + t_row;          // row & 3 == (row + 4) & 3
+      const int x = row & 3;
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int co = (((ks * 2) + (lane >> 5)) ^ sw) * 16;
-      bf16x8 a[4], b[2];
-      if (A_MN) {
-        const int row = ks * 16 + t_row;          // row & 3 == (row + 4) & 3
-        const int x = row & 3;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const char* p = cur + row * (kTile * 2) + ((t_chunk | ((i ^ x) << 2)) << 4) + t_byte;
-          const short4v lo = ds_read_tr(p);
-          const short4v hi = ds_read_tr(p + 4 * (kTile * 2));
-          const short4v v8[2] = {lo, hi};
-          a[i] = __builtin_bit_cast(bf16x8, v8);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a[i] = *reinterpret_cast<const bf16x8*>(cur + a_off + i * 32 * kRowBytes + co);
+      for (int i = 0; i < 4; ++i) {
+        const char* p = cur + row * (kTile * 2) + ((t_chunk | ((i ^ x) << 2)) << 4) + t_byte;
+        const short4v lo = ds_read_tr(p);
+        const short4v hi = ds_read_tr(p + 4 * (kTile * 2));
+        const short4v v8[2] = {lo, hi};
+        fa[buf][i] = __builtin_bit_cast(bf16x8, v8);
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(cur + b_off + j * 32 * kRowBytes + co);
+    } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        fa[buf][i] = *reinterpret_cast<const bf16x8*>(cur + a_off + i * 32 * kRowBytes + co);
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      fb[buf][j] = *reinterpret_cast<const bf16x8*>(cur + b_off + j * 32 * kRowBytes + co);
+  };
+  auto mfma = [&](int buf, int lo, int hi) {
+#pragma unroll
+    for (int q = lo; q < hi; ++q) {
+      const int i = q >> 1, j = q & 1;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  if (A_MN) stage_mn(A, 0, base); else stage(A, 0, base);
+  stage(B, 0, base + kOpBytes);
+  wait_vm<0>();
+  __syncthreads();
+  read_frags(0, 0, 0);
+
+  constexpr int kSteps = kBK / 16;
+  constexpr int kLast = (kSteps - 1) & 1;   // register set of the last step
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    const uint32_t nxt = base + ((kt + 1) & 1) * kStageBytes;
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ks = 0; ks < kSteps - 1; ++ks) {
+      // the other slice was freed by the barrier of the previous slice
+      if (more && ks == 0) {
+        if (A_MN) stage_mn(A, (kt + 1) * kBK, nxt); else stage(A, (kt + 1) * kBK, nxt);
+      }
+      if (more && ks == 1) stage(B, (kt + 1) * kBK, nxt + kOpBytes);
+      read_frags(kt, ks + 1, (ks + 1) & 1);
+      mfma(ks & 1, 0, 8);
+    }
+    mfma(kLast, 0, 4);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) {
+      // this wave's loads of slice kt + 1 are done; the barrier publishes
+      // everybody's and certifies that slice kt has been read by all waves
+      wait_vm<0>();
+      __syncthreads();
+      read_frags(kt + 1, 0, kLast ^ 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    mfma(kLast, 4, 8);
     __builtin_amdgcn_s_setprio(0);
   }
   __syncthreads();
