@@ -39,6 +39,28 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+def kernel_source_hash() -> str:
+    import hashlib
+    path = os.path.join(ROOT, "cross_entropy_amd", "csrc", "lmhead_kernels.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known size), or
+    None when the counters were taken on another version of the kernels."""
+    path = os.path.join(ROOT, "profiles", "lmhead_traffic_headline.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel") != kernel or t.get("kernels_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
 def cpu_baseline(h_bits, W_bits, targets, chunk, g_l, g_e, sample: int):
     """The fp64 oracle, as it stands, on `sample` tokens of the same inputs
     (forward + backward of those tokens; dW over them)."""
@@ -73,6 +95,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--cpu-sample", type=int, default=64, help="tokens the CPU oracle runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (5 times), the known-size "
+                         "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this head runs on a single MI355X and has no "
@@ -81,6 +106,16 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20)
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 5}), flush=True)
+        return 0
 
     import cross_entropy_amd as lm
     from cross_entropy_amd import _native
@@ -154,6 +189,9 @@ def main() -> int:
         achieved = dom["bytes"] / max(1, dom["launches"]) / (avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    traffic = stored_traffic(dom_name)
+    if traffic is not None:
+        roof["traffic"] = traffic
     roof["kernel"] = dom_name
     roof["avg_launch_ms"] = round(avg_ms, 4)
     roof["launches_per_step"] = dom["launches"] / args.steps
