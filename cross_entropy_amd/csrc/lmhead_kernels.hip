@@ -106,12 +106,15 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// One direct-to-LDS load: 64 lanes x 16 B land at m0 + 16 * lane. Issued as
-// inline asm so the compiler does not add a vmcnt(0) in front of every LDS
-// read of the ring; completion is awaited explicitly (wait_vm) before the
-// barrier that publishes a slice.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_wave_base)
+// One direct-to-LDS load: 64 lanes x 16 B land at m0 + 16 * lane; lane l
+// reads 16 bytes at sbase + voff(l) (scalar base, 32-bit per-lane offset,
+// so a wave's loads cost one VGPR each). Issued as inline asm so the
+// compiler does not add a vmcnt(0) in front of every LDS read of the ring;
+// completion is awaited explicitly (wait_vm) before the barrier that
+// publishes a slice.
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(lds_wave_base)
                : "memory");
 }
 
@@ -123,18 +126,20 @@ __device__ __forceinline__ void wait_vm() {
 
 // Stage rows [0, 256) x K [k0, k0 + 64) of one operand. Each wave loads 32
 // rows as 4 x 8 rows of 8 chunks; lane l fills physical chunk l % 8 of row
-// l / 8 with the logical chunk that the swizzle puts there.
+// l / 8 with the logical chunk that the swizzle puts there. Byte offsets
+// from op.base stay below 2^32: a tile spans 256 rows.
 __device__ __forceinline__ void stage(const Operand& op, int k0, uint32_t lds_op) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const char* b = reinterpret_cast<const char*>(op.base) + 2 * (int64_t)k0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r0 = wave * 32 + q * kRowsPerDma;
     const int r = r0 + (lane >> 3);
     const int c = (lane & 7) ^ swz(r);
     const int rr = min(r, op.rows - 1);
-    const uint16_t* g = op.base + (int64_t)rr * op.ld + k0 + c * 8;
-    dma16(g, __builtin_amdgcn_readfirstlane(lds_op + r0 * kRowBytes));
+    const uint32_t off = (uint32_t)((int64_t)rr * op.ld * 2) + (uint32_t)(c * 16);
+    dma16(off, b, __builtin_amdgcn_readfirstlane(lds_op + r0 * kRowBytes));
   }
 }
 
@@ -146,13 +151,14 @@ __device__ __forceinline__ void stage(const Operand& op, int k0, uint32_t lds_op
 __device__ __forceinline__ void stage_mn(const Operand& op, int k0, uint32_t lds_op) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const char* b = reinterpret_cast<const char*>(op.base + (int64_t)k0 * op.ld);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r0 = wave * 8 + q * 2;
     const int r = r0 + (lane >> 5);
     const int c = (lane & 31) ^ (4 * (r & 3));
-    const uint16_t* g = op.base + (int64_t)(k0 + r) * op.ld + c * 8;
-    dma16(g, __builtin_amdgcn_readfirstlane(lds_op + r0 * (kTile * 2)));
+    const uint32_t off = (uint32_t)((int64_t)r * op.ld * 2) + (uint32_t)(c * 16);
+    dma16(off, b, __builtin_amdgcn_readfirstlane(lds_op + r0 * (kTile * 2)));
   }
 }
 
@@ -169,6 +175,25 @@ __device__ __forceinline__ short4v ds_read_tr(const char* p) {
       (lds_s4)(const __attribute__((address_space(3))) char*)p);
 }
 
+// Scheduling pins. NM MFMAs of one 16-deep step with the NR LDS reads of the
+// next step spread between them, front-loaded: after MFMA q come
+// ceil((q+1) NR / NM) - ceil(q NR / NM) reads. The compiler's own order
+// issues the reads late and waits on them at once, which exposes the LDS
+// latency to the matrix pipe several times per slice.
+template <int NM, int NR, int Q>
+struct Pin {
+  static __device__ __forceinline__ void run() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    constexpr int n = ((Q + 1) * NR + NM - 1) / NM - (Q * NR + NM - 1) / NM;
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);   // n LDS reads
+    Pin<NM, NR, Q + 1>::run();
+  }
+};
+template <int NM, int NR>
+struct Pin<NM, NR, NM> {
+  static __device__ __forceinline__ void run() {}
+};
+
 // The tile core: acc[i][j] (wave sub-block i of 32 A-rows, j of 32 B-rows)
 // = sum over k < K of A[row][k] * B[row][k]. K is a multiple of 64. With
 // A_MN the A operand is MN-contiguous (see stage_mn) and its fragments are
@@ -176,12 +201,13 @@ __device__ __forceinline__ short4v ds_read_tr(const char* p) {
 // reused as soon as it returns.
 //
 // Schedule of one 64-deep slice k (4 steps of 16): the fragments of step
-// s + 1 are read into the other register set while the 8 MFMAs of step s
-// run; the loads of slice k + 1 are issued during steps 0 (A) and 1 (B);
-// the barrier that publishes slice k + 1 sits halfway through the MFMAs of
-// the last step, and the first fragments of slice k + 1 are read right
-// after it, behind the remaining MFMAs, so the matrix pipe never restarts
-// from an empty register set.
+// s + 1 are read into the other register set between the 8 MFMAs of step s
+// (pinned, in the order the MFMAs consume them); the loads of slice k + 1
+// are issued at the start of steps 0 (A) and 1 (B); the barrier that
+// publishes slice k + 1 sits halfway through the MFMAs of the last step, and
+// the first fragments of slice k + 1 are read right after it, between the
+// remaining MFMAs, so the matrix pipe never restarts from an empty register
+// set. The last slice is peeled off so the steady-state body has no branch.
 template <bool A_MN>
 __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int K, char* lds,
                                          f32x16 (&acc)[4][2]) {
@@ -210,28 +236,31 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
   const int t_byte = 8 * (sl & 1);
 
   bf16x8 fa[2][4], fb[2][2];
-  auto read_frags = [&](int slice, int ks, int buf) {
-    const char* cur = lds + (slice & 1) * kStageBytes;
-    const int co = (((ks * 2) + (lane >> 5)) ^ sw) * 16;
+  auto read_a = [&](const char* cur, int ks, int co, int buf, int i) {
     if (A_MN) {
       const int row = ks * 16 + t_row;          // row & 3 == (row + 4) & 3
       const int x = row & 3;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const char* p = cur + row * (kTile * 2) + ((t_chunk | ((i ^ x) << 2)) << 4) + t_byte;
-        const short4v lo = ds_read_tr(p);
-        const short4v hi = ds_read_tr(p + 4 * (kTile * 2));
-        const short4v v8[2] = {lo, hi};
-        fa[buf][i] = __builtin_bit_cast(bf16x8, v8);
-      }
+      const char* p = cur + row * (kTile * 2) + ((t_chunk | ((i ^ x) << 2)) << 4) + t_byte;
+      const short4v lo = ds_read_tr(p);
+      const short4v hi = ds_read_tr(p + 4 * (kTile * 2));
+      const short4v v8[2] = {lo, hi};
+      fa[buf][i] = __builtin_bit_cast(bf16x8, v8);
     } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[buf][i] = *reinterpret_cast<const bf16x8*>(cur + a_off + i * 32 * kRowBytes + co);
+      fa[buf][i] = *reinterpret_cast<const bf16x8*>(cur + a_off + i * 32 * kRowBytes + co);
     }
+  };
+  auto read_b = [&](const char* cur, int co, int buf, int j) {
+    fb[buf][j] = *reinterpret_cast<const bf16x8*>(cur + b_off + j * 32 * kRowBytes + co);
+  };
+  // in the order the MFMAs (i-major) consume them
+  auto read_frags = [&](int slice, int ks, int buf) {
+    const char* cur = lds + (slice & 1) * kStageBytes;
+    const int co = (((ks * 2) + (lane >> 5)) ^ sw) * 16;
+    read_a(cur, ks, co, buf, 0);
+    read_b(cur, co, buf, 0);
+    read_b(cur, co, buf, 1);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      fb[buf][j] = *reinterpret_cast<const bf16x8*>(cur + b_off + j * 32 * kRowBytes + co);
+    for (int i = 1; i < 4; ++i) read_a(cur, ks, co, buf, i);
   };
   auto mfma = [&](int buf, int lo, int hi) {
 #pragma unroll
@@ -240,6 +269,7 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
     }
   };
+  constexpr int kReads = A_MN ? 10 : 6;   // LDS read instructions per step
 
   if (A_MN) stage_mn(A, 0, base); else stage(A, 0, base);
   stage(B, 0, base + kOpBytes);
@@ -249,19 +279,22 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
 
   constexpr int kSteps = kBK / 16;
   constexpr int kLast = (kSteps - 1) & 1;   // register set of the last step
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
+  auto slice = [&](int kt, bool more) {
     const uint32_t nxt = base + ((kt + 1) & 1) * kStageBytes;
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < kSteps - 1; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
       // the other slice was freed by the barrier of the previous slice
       if (more && ks == 0) {
         if (A_MN) stage_mn(A, (kt + 1) * kBK, nxt); else stage(A, (kt + 1) * kBK, nxt);
       }
       if (more && ks == 1) stage(B, (kt + 1) * kBK, nxt + kOpBytes);
+      __builtin_amdgcn_sched_barrier(0);
       read_frags(kt, ks + 1, (ks + 1) & 1);
       mfma(ks & 1, 0, 8);
+      Pin<8, kReads, 0>::run();
+      __builtin_amdgcn_sched_barrier(0);
     }
     mfma(kLast, 0, 4);
     __builtin_amdgcn_s_setprio(0);
@@ -273,11 +306,14 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
       __syncthreads();
       read_frags(kt + 1, 0, kLast ^ 1);
     }
-    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
     mfma(kLast, 4, 8);
+    if (more) Pin<4, kReads, 0>::run();
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
-  }
+  };
+  for (int kt = 0; kt < nk - 1; ++kt) slice(kt, true);
+  slice(nk - 1, false);
   __syncthreads();
 }
 
