@@ -208,9 +208,21 @@ struct Pin<NM, NR, NM> {
 // the first fragments of slice k + 1 are read right after it, between the
 // remaining MFMAs, so the matrix pipe never restarts from an empty register
 // set. The last slice is peeled off so the steady-state body has no branch.
+//
+// Chaining tiles (the forward's walk over vocabulary tiles): `pipe` holds the
+// LDS slot of the tile's first slice and whether that slice was already
+// issued; with `next` the last slice issues the first slice of the next tile
+// (same operand shapes) into the free slot, so the next tile starts on data
+// that landed during this tile's epilogue.
+struct Pipe {
+  int slot = 0;         // LDS slot (0 or 1) of the first slice
+  bool staged = false;  // its loads were issued by the previous tile
+};
+
 template <bool A_MN>
 __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int K, char* lds,
-                                         f32x16 (&acc)[4][2]) {
+                                         f32x16 (&acc)[4][2], Pipe& pipe,
+                                         const Operand* nextA = nullptr, const Operand* nextB = nullptr) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1;
@@ -253,8 +265,9 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
     fb[buf][j] = *reinterpret_cast<const bf16x8*>(cur + b_off + j * 32 * kRowBytes + co);
   };
   // in the order the MFMAs (i-major) consume them
+  const int p0 = pipe.slot;
   auto read_frags = [&](int slice, int ks, int buf) {
-    const char* cur = lds + (slice & 1) * kStageBytes;
+    const char* cur = lds + ((p0 + slice) & 1) * kStageBytes;
     const int co = (((ks * 2) + (lane >> 5)) ^ sw) * 16;
     read_a(cur, ks, co, buf, 0);
     read_b(cur, co, buf, 0);
@@ -271,25 +284,33 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
   };
   constexpr int kReads = A_MN ? 10 : 6;   // LDS read instructions per step
 
-  if (A_MN) stage_mn(A, 0, base); else stage(A, 0, base);
-  stage(B, 0, base + kOpBytes);
+  if (!pipe.staged) {
+    const uint32_t first = base + p0 * kStageBytes;
+    if (A_MN) stage_mn(A, 0, first); else stage(A, 0, first);
+    stage(B, 0, first + kOpBytes);
+  }
   wait_vm<0>();
   __syncthreads();
   read_frags(0, 0, 0);
 
   constexpr int kSteps = kBK / 16;
   constexpr int kLast = (kSteps - 1) & 1;   // register set of the last step
+  const bool chain = nextA != nullptr;
   auto slice = [&](int kt, bool more) {
-    const uint32_t nxt = base + ((kt + 1) & 1) * kStageBytes;
+    const uint32_t nxt = base + ((p0 + kt + 1) & 1) * kStageBytes;
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < kSteps - 1; ++ks) {
       __builtin_amdgcn_sched_barrier(0);
-      // the other slice was freed by the barrier of the previous slice
+      // the other slot was freed by the barrier of the previous slice
       if (more && ks == 0) {
         if (A_MN) stage_mn(A, (kt + 1) * kBK, nxt); else stage(A, (kt + 1) * kBK, nxt);
       }
       if (more && ks == 1) stage(B, (kt + 1) * kBK, nxt + kOpBytes);
+      if (!more && chain && ks == 0) {
+        if (A_MN) stage_mn(*nextA, 0, nxt); else stage(*nextA, 0, nxt);
+      }
+      if (!more && chain && ks == 1) stage(*nextB, 0, nxt + kOpBytes);
       __builtin_amdgcn_sched_barrier(0);
       read_frags(kt, ks + 1, (ks + 1) & 1);
       mfma(ks & 1, 0, 8);
@@ -314,6 +335,8 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
   };
   for (int kt = 0; kt < nk - 1; ++kt) slice(kt, true);
   slice(nk - 1, false);
+  pipe.slot = (p0 + nk) & 1;
+  pipe.staged = chain;
   __syncthreads();
 }
 
@@ -375,11 +398,18 @@ __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
   }
 
   const Operand ob{hidden + (int64_t)tok0 * H, H, min(kTile, N - tok0)};
+  Pipe pipe;
   for (int vt = s; vt < n_vt; vt += S) {
     const int v0 = vt * kTile;
     const Operand oa{W + (int64_t)v0 * H, H, min(kTile, V - v0)};
     f32x16 acc[4][2];
-    mma_tile<false>(oa, ob, H, lds, acc);
+    if (vt + S < n_vt) {
+      const int v1 = v0 + S * kTile;
+      const Operand na{W + (int64_t)v1 * H, H, min(kTile, V - v1)};
+      mma_tile<false>(oa, ob, H, lds, acc, pipe, &na, &ob);
+    } else {
+      mma_tile<false>(oa, ob, H, lds, acc, pipe);
+    }
 
     const int vrow0 = v0 + wm * 128;
     if (vrow0 + 128 > V) {   // ragged last tile: rows past V take no part
@@ -510,7 +540,8 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
   const Operand oa{s.W + (int64_t)(v0 + vl0) * H, H, min(kTile, Vb - vl0)};
   const Operand ob{s.hidden + (int64_t)(t0 + tl0) * H, H, min(kTile, Ct - tl0)};
   f32x16 acc[4][2];
-  mma_tile<false>(oa, ob, H, lds, acc);
+  Pipe pipe;
+  mma_tile<false>(oa, ob, H, lds, acc, pipe);
 
   float nlseL[2], c0[2], c1[2], gl[2];
   int tr[2];
@@ -580,7 +611,8 @@ __device__ __forceinline__ void dw_tile(const BwdStep& s, int vid, char* lds) {
   const Operand oa{s.g_dz + m0, s.ld_dz, kTile};
   const Operand ob{s.ht + (int64_t)h0 * s.ld_ht + s.g_t0, s.ld_ht, kTile};
   f32x16 acc[4][2];
-  mma_tile<true>(oa, ob, (s.g_Ct + kBK - 1) / kBK * kBK, lds, acc);
+  Pipe pipe;
+  mma_tile<true>(oa, ob, (s.g_Ct + kBK - 1) / kBK * kBK, lds, acc, pipe);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -613,7 +645,8 @@ __device__ __forceinline__ void dh_tile(const BwdStep& s, int vid, char* lds) {
   const Operand oa{s.g_dz + (int64_t)m0 * s.ld_dz, s.ld_dz, kTile};
   const Operand ob{s.Wt + (int64_t)h0 * s.ld_wt + s.g_v0, s.ld_wt, kTile};
   f32x16 acc[4][2];
-  mma_tile<false>(oa, ob, (s.g_Vb + kBK - 1) / kBK * kBK, lds, acc);
+  Pipe pipe;
+  mma_tile<false>(oa, ob, (s.g_Vb + kBK - 1) / kBK * kBK, lds, acc, pipe);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
