@@ -11,6 +11,9 @@ unshifted textbook definitions and pins that oracle in ``tests/``.
   differences at step 1e-20 in 60-digit arithmetic (error ~1e-38, far below
   float64 resolution).
 
+Temperature T (default 1) divides every logit: z_v = (h . W_v) / T, with T
+given as a decimal string and held exactly.
+
 Inputs are exact: bf16 values are dyadic rationals, which Decimal holds
 exactly. Only for N <= 4, H <= 8, V <= 16 or so: every derivative costs two
 full evaluations.
@@ -45,10 +48,10 @@ def _matrix(bits_rows):
     return [[bf16_bits_to_decimal(b) for b in row] for row in bits_rows]
 
 
-def _token(h_row, W, t):
+def _token(h_row, W, t, T=Decimal(1)):
     """(logp, entropy, lse) of one token from Decimal rows."""
     V = len(W)
-    z = [sum(a * b for a, b in zip(h_row, W[v])) for v in range(V)]
+    z = [sum(a * b for a, b in zip(h_row, W[v])) / T for v in range(V)]
     ez = [x.exp() for x in z]
     s = sum(ez)
     p = [e / s for e in ez]
@@ -58,10 +61,11 @@ def _token(h_row, W, t):
     return logp, ent, lse
 
 
-def forward(hidden_bits, W_bits, targets):
+def forward(hidden_bits, W_bits, targets, temperature: str = "1"):
     """Per-token (logp, entropy, lse) as Decimals; masked tokens give zeros."""
     with localcontext() as ctx:
         ctx.prec = _PREC
+        T = Decimal(temperature)
         h = _matrix(hidden_bits)
         W = _matrix(W_bits)
         V = len(W)
@@ -69,13 +73,13 @@ def forward(hidden_bits, W_bits, targets):
         for i, t in enumerate(targets):
             t = int(t)
             if 0 <= t < V:
-                out.append(_token(h[i], W, t))
+                out.append(_token(h[i], W, t, T))
             else:
                 out.append((Decimal(0), Decimal(0), Decimal(0)))
         return out
 
 
-def loss(h, W, targets, g_logp, g_ent):
+def loss(h, W, targets, g_logp, g_ent, T=Decimal(1)):
     """L on Decimal matrices (masked tokens add nothing)."""
     V = len(W)
     total = Decimal(0)
@@ -83,15 +87,16 @@ def loss(h, W, targets, g_logp, g_ent):
         t = int(t)
         if not (0 <= t < V):
             continue
-        logp, ent, _ = _token(h[i], W, t)
+        logp, ent, _ = _token(h[i], W, t, T)
         total += Decimal(repr(float(g_logp[i]))) * logp + Decimal(repr(float(g_ent[i]))) * ent
     return total
 
 
-def gradients(hidden_bits, W_bits, targets, g_logp, g_ent, step: str = "1e-20"):
+def gradients(hidden_bits, W_bits, targets, g_logp, g_ent, step: str = "1e-20", temperature: str = "1"):
     """(dh, dW) as nested lists of Decimals by central differences of L."""
     with localcontext() as ctx:
         ctx.prec = _PREC
+        T = Decimal(temperature)
         h = _matrix(hidden_bits)
         W = _matrix(W_bits)
         d = Decimal(step)
@@ -99,9 +104,9 @@ def gradients(hidden_bits, W_bits, targets, g_logp, g_ent, step: str = "1e-20"):
         def central(mat, r, c):
             keep = mat[r][c]
             mat[r][c] = keep + d
-            up = loss(h, W, targets, g_logp, g_ent)
+            up = loss(h, W, targets, g_logp, g_ent, T)
             mat[r][c] = keep - d
-            dn = loss(h, W, targets, g_logp, g_ent)
+            dn = loss(h, W, targets, g_logp, g_ent, T)
             mat[r][c] = keep
             return (up - dn) / (2 * d)
 

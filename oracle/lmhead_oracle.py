@@ -30,6 +30,14 @@ of the chunk with hidden row h_i and target id t_i:
 5. backward of L = sum_i g_logp_i * logp_i + g_ent_i * entropy_i:
    dz = g_logp (onehot(t) - p) - g_ent p (log p + entropy), log p = z - lse;
    dh_i = W^T dz; dW += dz h_i^T.
+
+Temperature T > 0 (default 1): the head scores the tempered logits z / T,
+so every statistic above is that of softmax(z / T), and the backward divides
+the tempered logits' cotangent by T before both gradient matmuls (chain rule
+through z / T).
+   [tunix #2913 runs its head tests at temperatures 1 and 0.7 and lists
+   "the backward's temperature division dropped" among the broken copies
+   its tests must catch.]
    [tunix #2913: the logits' cotangent in one elementwise pass over the
    recomputed logits when only the log-probs carry a cotangent; a loss that
    differentiates the entropy adds the entropy term; both gradient matmuls
@@ -90,6 +98,16 @@ def _logits(h_rows: np.ndarray, W: np.ndarray) -> np.ndarray:
     return h_rows @ W.T
 
 
+def _temper(z: np.ndarray, temperature: float) -> np.ndarray:
+    """The tempered logits z / T that the head scores."""
+    return z / temperature
+
+
+def _raw_cotangent(dz: np.ndarray, temperature: float) -> np.ndarray:
+    """Chain rule through z / T: the untempered logits' cotangent is dz / T."""
+    return dz / temperature
+
+
 def _log_sum_exp(z: np.ndarray) -> np.ndarray:
     """Step 3: lse = m + log(sum exp(z - m)) per row."""
     m = np.max(z, axis=1, keepdims=True)
@@ -118,8 +136,15 @@ def _cotangent(z, lse, p, ent, t, g_l, g_e) -> np.ndarray:
     return dz
 
 
-def _rows_stats(h_rows, W, t):
-    z = _logits(h_rows, W)
+def _check_temperature(temperature):
+    T = float(temperature)
+    if not (np.isfinite(T) and T > 0.0):
+        raise ValueError("temperature must be finite and > 0")
+    return T
+
+
+def _rows_stats(h_rows, W, t, temperature=1.0):
+    z = _temper(_logits(h_rows, W), temperature)
     lse = _log_sum_exp(z)
     p = _probs(z, lse)
     logp = _target_logit(z, t) - lse
@@ -144,7 +169,7 @@ def _token_blocks(lo: int, hi: int, row_block: int):
 
 
 def forward(hidden_bits, W_bits, targets, chunk_size: int, tokens: Optional[np.ndarray] = None,
-            row_block: int = 256):
+            row_block: int = 256, temperature: float = 1.0):
     """Forward values (logp, entropy, lse), float64 arrays.
 
     ``tokens``: optional sorted index subset; then only those tokens are
@@ -152,6 +177,7 @@ def forward(hidden_bits, W_bits, targets, chunk_size: int, tokens: Optional[np.n
     ``len(tokens)`` entries. ``row_block`` only sets how many tokens of a
     chunk are evaluated per numpy call; the values do not depend on it.
     """
+    T = _check_temperature(temperature)
     h, W, t = _prepare(hidden_bits, W_bits, targets)
     N, V = h.shape[0], W.shape[0]
     ids = np.arange(N) if tokens is None else np.asarray(tokens, dtype=np.int64)
@@ -165,14 +191,14 @@ def forward(hidden_bits, W_bits, targets, chunk_size: int, tokens: Optional[np.n
         sel = sel[valid[sel]]
         for b0 in range(0, sel.shape[0], row_block):
             rows = sel[b0:b0 + row_block]
-            _, l, _, lp, en = _rows_stats(h[rows], W, t[rows])
+            _, l, _, lp, en = _rows_stats(h[rows], W, t[rows], T)
             out = rows if pos is None else np.array([pos[int(i)] for i in rows], dtype=np.int64)
             logp[out], ent[out], lse[out] = lp, en, l
     return logp, ent, lse
 
 
 def backward(hidden_bits, W_bits, targets, chunk_size: int, g_logp=None, g_ent=None,
-             tokens: Optional[np.ndarray] = None, row_block: int = 256):
+             tokens: Optional[np.ndarray] = None, row_block: int = 256, temperature: float = 1.0):
     """Gradients (dh, dW) of L = sum_i g_logp_i logp_i + g_ent_i entropy_i.
 
     ``g_logp`` / ``g_ent`` of None mean zero. dh is [N, H] (or
@@ -181,6 +207,7 @@ def backward(hidden_bits, W_bits, targets, chunk_size: int, g_logp=None, g_ent=N
     dW exactly when every other token's cotangents are zero.
     Masked tokens give dh rows of 0 and nothing to dW, whatever their hidden
     row holds (they are never multiplied, only skipped)."""
+    T = _check_temperature(temperature)
     h, W, t = _prepare(hidden_bits, W_bits, targets)
     N, H = h.shape
     V = W.shape[0]
@@ -196,8 +223,8 @@ def backward(hidden_bits, W_bits, targets, chunk_size: int, g_logp=None, g_ent=N
         sel = sel[valid[sel]]
         for b0 in range(0, sel.shape[0], row_block):
             rows = sel[b0:b0 + row_block]
-            z, l, p, _, en = _rows_stats(h[rows], W, t[rows])
-            dz = _cotangent(z, l, p, en, t[rows], g_l[rows], g_e[rows])
+            z, l, p, _, en = _rows_stats(h[rows], W, t[rows], T)
+            dz = _raw_cotangent(_cotangent(z, l, p, en, t[rows], g_l[rows], g_e[rows]), T)
             out = rows if pos is None else np.array([pos[int(i)] for i in rows], dtype=np.int64)
             dh[out] = dz @ W
             dW += dz.T @ h[rows]
@@ -205,23 +232,24 @@ def backward(hidden_bits, W_bits, targets, chunk_size: int, g_logp=None, g_ent=N
 
 
 def forward_backward(hidden_bits, W_bits, targets, chunk_size: int, g_logp=None, g_ent=None,
-                     tokens: Optional[np.ndarray] = None, row_block: int = 256):
+                     tokens: Optional[np.ndarray] = None, row_block: int = 256, temperature: float = 1.0):
     """Both passes; returns dict(logp, entropy, lse, dh, dW)."""
-    logp, ent, lse = forward(hidden_bits, W_bits, targets, chunk_size, tokens, row_block)
-    dh, dW = backward(hidden_bits, W_bits, targets, chunk_size, g_logp, g_ent, tokens, row_block)
+    logp, ent, lse = forward(hidden_bits, W_bits, targets, chunk_size, tokens, row_block, temperature)
+    dh, dW = backward(hidden_bits, W_bits, targets, chunk_size, g_logp, g_ent, tokens, row_block, temperature)
     return {"logp": logp, "entropy": ent, "lse": lse, "dh": dh, "dW": dW}
 
 
-def loss(hidden_f64: np.ndarray, W_f64: np.ndarray, targets, g_logp, g_ent) -> float:
+def loss(hidden_f64: np.ndarray, W_f64: np.ndarray, targets, g_logp, g_ent, temperature: float = 1.0) -> float:
     """L = sum_i g_logp_i logp_i + g_ent_i entropy_i on float64 inputs (for
     finite-difference checks of ``backward``); masked tokens add nothing."""
+    T = _check_temperature(temperature)
     t = np.asarray(targets, dtype=np.int64)
     V = W_f64.shape[0]
     valid = valid_targets(t, V)
     rows = np.flatnonzero(valid)
     if rows.size == 0:
         return 0.0
-    _, _, _, lp, en = _rows_stats(hidden_f64[rows], W_f64, t[rows])
+    _, _, _, lp, en = _rows_stats(hidden_f64[rows], W_f64, t[rows], T)
     g_l = np.asarray(g_logp, dtype=np.float64)[rows]
     g_e = np.asarray(g_ent, dtype=np.float64)[rows]
     return float(np.sum(g_l * lp) + np.sum(g_e * en))

@@ -277,6 +277,86 @@ def pin_subset_evaluation():
     _close(dW_s, sparse_full[1], 1e-13, 1e-15, what="subset dW")
 
 
+# --- temperature ------------------------------------------------------------------
+# tunix #2913 tests its head at temperatures 1 and 0.7; the tempered head
+# scores z / T and divides the backward's cotangent by T.
+
+def _scaled_bits(bits, factor):
+    return bf16(f64(bits) * factor)
+
+
+def pin_temperature_power_of_two():
+    """T = 2^k scores exactly what T = 1 scores with W scaled by 2^-k (exact in
+    bf16 for normal values): same statistics and dh, and dW(T) = 2^-k dW(W 2^-k)
+    by the chain rule through W / T."""
+    h, W, t, g_l, g_e = _rand_case(11, 9, 8, 13, w_std=0.5, n_masked=2)
+    for k in (1, -1, 3):
+        T = 2.0 ** k
+        Ws = _scaled_bits(W, 2.0 ** -k)
+        assert np.array_equal(f64(Ws), f64(W) * 2.0 ** -k), "scaling by a power of two must be exact"
+        a = O.forward_backward(h, W, t, 4, g_l, g_e, temperature=T)
+        b = O.forward_backward(h, Ws, t, 4, g_l, g_e)
+        for key in ("logp", "entropy", "lse", "dh"):
+            _close(a[key], b[key], 1e-13, 1e-15, what=f"T={T} {key} vs scaled W")
+        _close(a["dW"], b["dW"] * 2.0 ** -k, 1e-12, 1e-15, what=f"T={T} dW vs scaled W")
+
+
+def pin_temperature_bruteforce():
+    """T = 0.7: fp64 oracle vs the 50-digit unshifted definitions, forward and
+    central-difference gradients."""
+    h, W, t, g_l, g_e = _bruteforce_case()
+    logp, ent, lse = O.forward(h, W, t, 2, temperature=0.7)
+    ref = B.forward(h.tolist(), W.tolist(), t.tolist(), temperature="0.7")
+    for i, (lp, en, ls) in enumerate(ref):
+        _close(logp[i], float(lp), 1e-13, 1e-15, what=f"T=0.7 logp[{i}] vs brute force")
+        _close(ent[i], float(en), 1e-13, 1e-15, what=f"T=0.7 entropy[{i}] vs brute force")
+        _close(lse[i], float(ls), 1e-13, 1e-15, what=f"T=0.7 lse[{i}] vs brute force")
+    dh, dW = O.backward(h, W, t, 2, g_l, g_e, temperature=0.7)
+    rdh, rdW = B.gradients(h.tolist(), W.tolist(), t.tolist(), g_l, g_e, temperature="0.7")
+    rdh = np.array([[float(x) for x in row] for row in rdh])
+    rdW = np.array([[float(x) for x in row] for row in rdW])
+    _close(dh, rdh, 1e-11, 1e-13 * np.abs(rdh).max(), what="T=0.7 dh vs brute-force differences")
+    _close(dW, rdW, 1e-11, 1e-13 * np.abs(rdW).max(), what="T=0.7 dW vs brute-force differences")
+
+
+def pin_temperature_fd():
+    """T = 0.7: fp64 central differences of the tempered loss vs the backward."""
+    N, H, V = 4, 5, 6
+    h, W, t, g_l, g_e = _rand_case(12, N, H, V, w_std=0.6)
+    t[2] = -1
+    hf, Wf = f64(h), f64(W)
+    dh, dW = O.backward(h, W, t, 3, g_l, g_e, temperature=0.7)
+    eps = 1e-6
+    for mat, grad, name in ((hf, dh, "dh"), (Wf, dW, "dW")):
+        num = np.zeros_like(mat)
+        for idx in np.ndindex(mat.shape):
+            keep = mat[idx]
+            mat[idx] = keep + eps
+            up = O.loss(hf, Wf, t, g_l, g_e, temperature=0.7)
+            mat[idx] = keep - eps
+            dn = O.loss(hf, Wf, t, g_l, g_e, temperature=0.7)
+            mat[idx] = keep
+            num[idx] = (up - dn) / (2 * eps)
+        _close(grad, num, 1e-7, 1e-8, what=f"T=0.7 {name} vs central differences")
+
+
+def pin_temperature_limit():
+    """T -> infinity flattens the distribution: logp -> -ln V, entropy -> ln V,
+    lse - ln V -> mean(z) / T; the gradients vanish like 1 / T."""
+    h, W, t, g_l, g_e = _rand_case(13, 6, 8, 11, w_std=0.5)
+    V = W.shape[0]
+    T = 1e9
+    r = O.forward_backward(h, W, t, 4, g_l, g_e, temperature=T)
+    z = f64(h) @ f64(W).T
+    _close(r["logp"], np.full(6, -math.log(V)), 0.0, 1e-8, what="T->inf logp")
+    _close(r["entropy"], np.full(6, math.log(V)), 0.0, 1e-8, what="T->inf entropy")
+    _close(r["lse"] - math.log(V), z.mean(axis=1) / T, 1e-6, 1e-15, what="T->inf lse - ln V")
+    # dh_i -> (g_l (W[t_i] - mean W)) / T at uniform p (the entropy term vanishes)
+    Wf = f64(W)
+    ref_dh = g_l[:, None] * (Wf[t] - Wf.mean(axis=0)[None, :]) / T
+    _close(r["dh"], ref_dh, 1e-6, 1e-20, what="T->inf dh")
+
+
 ALL_PINS = [
     pin_W_zero,
     pin_h_zero,
@@ -290,4 +370,8 @@ ALL_PINS = [
     pin_masking,
     pin_chunk_invariance,
     pin_subset_evaluation,
+    pin_temperature_power_of_two,
+    pin_temperature_bruteforce,
+    pin_temperature_fd,
+    pin_temperature_limit,
 ]

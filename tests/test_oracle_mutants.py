@@ -6,7 +6,9 @@ The mistake list follows the kinds of broken copies google/tunix pull request
 #2913 reports catching in its fused-head tests (cotangent sign flipped, max
 dropped from the log-probs, max and exp-sum swapped, entropy sign flipped,
 vocabulary bound off by one, wrap of negative ids, isfinite mask dropped),
-plus transposed operands and dropped terms."""
+plus transposed operands and dropped terms, and the tempered head's
+mistakes (temperature ignored or multiplied, the backward's division by the
+temperature dropped)."""
 import numpy as np
 import pytest
 
@@ -81,6 +83,18 @@ def _m_probs_unnormalised(z, lse):
     return np.exp(z - np.max(z, axis=1, keepdims=True))
 
 
+def _m_temperature_ignored(z, temperature):
+    return z
+
+
+def _m_temperature_multiplied(z, temperature):
+    return z * temperature
+
+
+def _m_backward_temperature_division_dropped(dz, temperature):
+    return dz
+
+
 _orig = {}
 
 MUTANTS = {
@@ -98,6 +112,9 @@ MUTANTS = {
     "target_logit_wrong_index": ("_target_logit", _m_target_logit_first_row),
     "logits_scaled": ("_logits", _m_logits_transposed_scale),
     "probs_unnormalised": ("_probs", _m_probs_unnormalised),
+    "temperature_ignored": ("_temper", _m_temperature_ignored),
+    "temperature_multiplied": ("_temper", _m_temperature_multiplied),
+    "backward_temperature_division_dropped": ("_raw_cotangent", _m_backward_temperature_division_dropped),
 }
 
 
