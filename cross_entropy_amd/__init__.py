@@ -12,7 +12,10 @@ Entry points mirror the C ABI:
     lmhead_logps_fwd(hidden, W, targets, chunk_size, logp, entropy, lse, workspace)
     lmhead_logps_bwd(hidden, W, targets, chunk_size, lse, entropy, g_logp, g_ent,
                      dh, dW, workspace)
-and two allocating helpers, ``forward`` and ``backward``.
+    lmhead_logps_fwd_temp / lmhead_logps_bwd_temp   (the same with a temperature
+                     after chunk_size: the head scores the logits divided by it)
+and two allocating helpers, ``forward`` and ``backward`` (``temperature=``
+selects the tempered calls).
 """
 from __future__ import annotations
 
@@ -26,6 +29,8 @@ __all__ = [
     "lmhead_logps_workspace_bytes",
     "lmhead_logps_fwd",
     "lmhead_logps_bwd",
+    "lmhead_logps_fwd_temp",
+    "lmhead_logps_bwd_temp",
     "forward",
     "backward",
     "version",
@@ -86,16 +91,17 @@ def _shapes(hidden, W, targets):
     return int(N), int(H), int(V)
 
 
-def lmhead_logps_fwd(hidden, W, targets, chunk_size: int, logp, entropy, lse, workspace, stream=None) -> None:
-    """Enqueue the forward on ``stream`` (default: torch's current stream)."""
+def _fwd_args(hidden, W, targets, chunk_size, logp, entropy, lse, workspace, stream):
     torch = _torch()
     N, H, V = _shapes(hidden, W, targets)
     dev = hidden.device
-    args = (
+    ptrs = (
         _ptr(hidden, "hidden", _bf16_types(), dev),
         _ptr(W, "W", _bf16_types(), dev),
         _ptr(targets, "targets", (torch.int32,), dev),
         N, H, V, chunk_size,
+    )
+    outs = (
         _ptr(logp, "logp", (torch.float32,), dev, N),
         _ptr(entropy, "entropy", (torch.float32,), dev, N, optional=True),
         _ptr(lse, "lse", (torch.float32,), dev, N),
@@ -103,22 +109,35 @@ def lmhead_logps_fwd(hidden, W, targets, chunk_size: int, logp, entropy, lse, wo
         workspace.numel(),
         _stream(dev, stream),
     )
-    _native.check(_native.raw_fwd(*args))
+    return ptrs, outs
 
 
-def lmhead_logps_bwd(hidden, W, targets, chunk_size: int, lse, entropy, g_logp, g_ent, dh, dW, workspace,
-                     stream=None) -> None:
-    """Enqueue the backward on ``stream`` (default: torch's current stream)."""
+def lmhead_logps_fwd(hidden, W, targets, chunk_size: int, logp, entropy, lse, workspace, stream=None) -> None:
+    """Enqueue the forward on ``stream`` (default: torch's current stream)."""
+    ptrs, outs = _fwd_args(hidden, W, targets, chunk_size, logp, entropy, lse, workspace, stream)
+    _native.check(_native.raw_fwd(*ptrs, *outs))
+
+
+def lmhead_logps_fwd_temp(hidden, W, targets, chunk_size: int, temperature: float, logp, entropy, lse, workspace,
+                          stream=None) -> None:
+    """Enqueue the tempered forward (logits / temperature) on ``stream``."""
+    ptrs, outs = _fwd_args(hidden, W, targets, chunk_size, logp, entropy, lse, workspace, stream)
+    _native.check(_native.raw_fwd_temp(*ptrs, temperature, *outs))
+
+
+def _bwd_args(hidden, W, targets, chunk_size, lse, entropy, g_logp, g_ent, dh, dW, workspace, stream):
     torch = _torch()
     N, H, V = _shapes(hidden, W, targets)
     dev = hidden.device
     if tuple(dh.shape) != (N, H) or tuple(dW.shape) != (V, H):
         raise ValueError("dh must be [N,H] and dW [V,H]")
-    args = (
+    ptrs = (
         _ptr(hidden, "hidden", _bf16_types(), dev),
         _ptr(W, "W", _bf16_types(), dev),
         _ptr(targets, "targets", (torch.int32,), dev),
         N, H, V, chunk_size,
+    )
+    rest = (
         _ptr(lse, "lse", (torch.float32,), dev, N),
         _ptr(entropy, "entropy", (torch.float32,), dev, N, optional=True),
         _ptr(g_logp, "g_logp", (torch.float32,), dev, N, optional=True),
@@ -129,7 +148,22 @@ def lmhead_logps_bwd(hidden, W, targets, chunk_size: int, lse, entropy, g_logp, 
         workspace.numel(),
         _stream(dev, stream),
     )
-    _native.check(_native.raw_bwd(*args))
+    return ptrs, rest
+
+
+def lmhead_logps_bwd(hidden, W, targets, chunk_size: int, lse, entropy, g_logp, g_ent, dh, dW, workspace,
+                     stream=None) -> None:
+    """Enqueue the backward on ``stream`` (default: torch's current stream)."""
+    ptrs, rest = _bwd_args(hidden, W, targets, chunk_size, lse, entropy, g_logp, g_ent, dh, dW, workspace, stream)
+    _native.check(_native.raw_bwd(*ptrs, *rest))
+
+
+def lmhead_logps_bwd_temp(hidden, W, targets, chunk_size: int, temperature: float, lse, entropy, g_logp, g_ent,
+                          dh, dW, workspace, stream=None) -> None:
+    """Enqueue the tempered backward on ``stream``; lse and entropy come from
+    the tempered forward with the same temperature."""
+    ptrs, rest = _bwd_args(hidden, W, targets, chunk_size, lse, entropy, g_logp, g_ent, dh, dW, workspace, stream)
+    _native.check(_native.raw_bwd_temp(*ptrs, temperature, *rest))
 
 
 def workspace_for(hidden, W, chunk_size: int, with_backward: bool = True):
@@ -141,8 +175,9 @@ def workspace_for(hidden, W, chunk_size: int, with_backward: bool = True):
 
 
 def forward(hidden, W, targets, chunk_size: int, with_entropy: bool = True, workspace=None,
-            stream=None) -> Tuple:
-    """Allocate outputs (torch) and run the forward: (logp, entropy | None, lse)."""
+            stream=None, temperature: Optional[float] = None) -> Tuple:
+    """Allocate outputs (torch) and run the forward: (logp, entropy | None, lse).
+    ``temperature`` (None: the untempered call) scores the logits divided by it."""
     torch = _torch()
     N = hidden.shape[0]
     dev = hidden.device
@@ -151,13 +186,17 @@ def forward(hidden, W, targets, chunk_size: int, with_entropy: bool = True, work
     ent = torch.empty(N, dtype=torch.float32, device=dev) if with_entropy else None
     if workspace is None:
         workspace = workspace_for(hidden, W, chunk_size, with_backward=False)
-    lmhead_logps_fwd(hidden, W, targets, chunk_size, logp, ent, lse, workspace, stream)
+    if temperature is None:
+        lmhead_logps_fwd(hidden, W, targets, chunk_size, logp, ent, lse, workspace, stream)
+    else:
+        lmhead_logps_fwd_temp(hidden, W, targets, chunk_size, temperature, logp, ent, lse, workspace, stream)
     return logp, ent, lse
 
 
 def backward(hidden, W, targets, chunk_size: int, lse, entropy, g_logp, g_ent: Optional = None,
-             workspace=None, stream=None) -> Tuple:
-    """Allocate gradients (torch) and run the backward: (dh, dW), float32."""
+             workspace=None, stream=None, temperature: Optional[float] = None) -> Tuple:
+    """Allocate gradients (torch) and run the backward: (dh, dW), float32.
+    ``temperature`` must match the forward that produced lse and entropy."""
     torch = _torch()
     N, H = hidden.shape
     V = W.shape[0]
@@ -166,5 +205,9 @@ def backward(hidden, W, targets, chunk_size: int, lse, entropy, g_logp, g_ent: O
     dW = torch.empty((V, H), dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = workspace_for(hidden, W, chunk_size, with_backward=True)
-    lmhead_logps_bwd(hidden, W, targets, chunk_size, lse, entropy, g_logp, g_ent, dh, dW, workspace, stream)
+    if temperature is None:
+        lmhead_logps_bwd(hidden, W, targets, chunk_size, lse, entropy, g_logp, g_ent, dh, dW, workspace, stream)
+    else:
+        lmhead_logps_bwd_temp(hidden, W, targets, chunk_size, temperature, lse, entropy, g_logp, g_ent, dh, dW,
+                              workspace, stream)
     return dh, dW

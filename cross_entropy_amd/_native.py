@@ -26,6 +26,8 @@ EXPORTED = (
     "lmhead_logps_workspace_bytes",
     "lmhead_logps_fwd",
     "lmhead_logps_bwd",
+    "lmhead_logps_fwd_temp",
+    "lmhead_logps_bwd_temp",
     "lmhead_logps_last_error",
     "lmhead_logps_version",
     "lmhead_logps_trace_enable",
@@ -80,6 +82,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lmhead_logps_fwd.restype = ctypes.c_int
     lib.lmhead_logps_bwd.argtypes = [p, p, p, i64, i64, i64, i64, p, p, p, p, p, p, p, sz, p]
     lib.lmhead_logps_bwd.restype = ctypes.c_int
+    f32 = ctypes.c_float
+    lib.lmhead_logps_fwd_temp.argtypes = [p, p, p, i64, i64, i64, i64, f32, p, p, p, p, sz, p]
+    lib.lmhead_logps_fwd_temp.restype = ctypes.c_int
+    lib.lmhead_logps_bwd_temp.argtypes = [p, p, p, i64, i64, i64, i64, f32, p, p, p, p, p, p, p, sz, p]
+    lib.lmhead_logps_bwd_temp.restype = ctypes.c_int
     lib.lmhead_logps_last_error.argtypes = []
     lib.lmhead_logps_last_error.restype = ctypes.c_char_p
     lib.lmhead_logps_version.argtypes = []
@@ -123,6 +130,23 @@ def raw_bwd(hidden, W, targets, N, H, V, chunk_size, lse, entropy, g_logp, g_ent
                                    int(chunk_size), lse or None, entropy or None, g_logp or None,
                                    g_ent or None, dh or None, dW or None, workspace or None,
                                    int(workspace_bytes), stream or None)
+
+
+def raw_fwd_temp(hidden, W, targets, N, H, V, chunk_size, temperature, logp, entropy, lse, workspace,
+                 workspace_bytes, stream) -> int:
+    """Call lmhead_logps_fwd_temp with integer addresses (0 = NULL); returns the status."""
+    return load().lmhead_logps_fwd_temp(hidden or None, W or None, targets or None, int(N), int(H), int(V),
+                                        int(chunk_size), float(temperature), logp or None, entropy or None,
+                                        lse or None, workspace or None, int(workspace_bytes), stream or None)
+
+
+def raw_bwd_temp(hidden, W, targets, N, H, V, chunk_size, temperature, lse, entropy, g_logp, g_ent, dh, dW,
+                 workspace, workspace_bytes, stream) -> int:
+    """Call lmhead_logps_bwd_temp with integer addresses (0 = NULL); returns the status."""
+    return load().lmhead_logps_bwd_temp(hidden or None, W or None, targets or None, int(N), int(H), int(V),
+                                        int(chunk_size), float(temperature), lse or None, entropy or None,
+                                        g_logp or None, g_ent or None, dh or None, dW or None,
+                                        workspace or None, int(workspace_bytes), stream or None)
 
 
 TRACE_KERNELS = ("fwd_stats_kernel", "fwd_merge_kernel", "bwd_step_kernel", "transpose_kernel",

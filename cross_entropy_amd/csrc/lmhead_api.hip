@@ -144,6 +144,21 @@ int check_shape(int64_t N, int64_t H, int64_t V, int64_t chunk_size) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Base-2 scale of the tempered logits and the reciprocal temperature; at
+// T = 1 these are log2(e) and 1 exactly, so the untempered entry points give
+// the same bits as the tempered ones at T = 1.
+float temper_scale(float temperature) { return (float)(1.4426950408889634 / (double)temperature); }
+float inv_temperature(float temperature) { return (float)(1.0 / (double)temperature); }
+
+int check_temperature(float temperature) {
+  if (!(std::isfinite(temperature) && temperature > 0.0f))
+    return fail(LMH_ERR_ARGS, "temperature must be finite and > 0, got %g", (double)temperature);
+  if (!std::isfinite(temper_scale(temperature)) || !std::isfinite(inv_temperature(temperature)))
+    return fail(LMH_ERR_ARGS, "temperature %g is too small: 1 / temperature overflows float32",
+                (double)temperature);
+  return LMH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -163,10 +178,13 @@ int lmhead_logps_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t chunk_
   return ok();
 }
 
-int lmhead_logps_fwd(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, int64_t N,
-                     int64_t H, int64_t V, int64_t chunk_size, float* logp, float* entropy,
-                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+int lmhead_logps_fwd_temp(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
+                          int64_t N, int64_t H, int64_t V, int64_t chunk_size, float temperature,
+                          float* logp, float* entropy, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   int rc = check_shape(N, H, V, chunk_size);
+  if (rc != LMH_OK) return rc;
+  rc = check_temperature(temperature);
   if (rc != LMH_OK) return rc;
   if (N == 0) return ok();
   if (!hidden || !W || !targets || !logp || !lse || !workspace)
@@ -177,18 +195,22 @@ int lmhead_logps_fwd(const uint16_t* hidden, const uint16_t* W, const int32_t* t
   const lmh::FwdPlan p = lmh::plan_forward(N, H, V);
   if (workspace_bytes < p.bytes)
     return fail(LMH_ERR_WORKSPACE, "fwd: workspace of %zu bytes, %zu needed", workspace_bytes, p.bytes);
-  lmh::FwdArgs a{hidden, W, targets, N, H, V, p.S, p.n_tt, p.n_vt, workspace, p.part_ld,
+  lmh::FwdArgs a{hidden, W, targets, N, H, V, p.S, p.n_tt, p.n_vt,
+                 temper_scale(temperature), inv_temperature(temperature), workspace, p.part_ld,
                  logp, entropy, lse};
   const hipError_t e = lmh::launch_fwd(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(LMH_ERR_HIP, "fwd: launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
-int lmhead_logps_bwd(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, int64_t N,
-                     int64_t H, int64_t V, int64_t chunk_size, const float* lse,
-                     const float* entropy, const float* g_logp, const float* g_ent, float* dh,
-                     float* dW, void* workspace, size_t workspace_bytes, void* stream) {
+int lmhead_logps_bwd_temp(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
+                          int64_t N, int64_t H, int64_t V, int64_t chunk_size, float temperature,
+                          const float* lse, const float* entropy, const float* g_logp,
+                          const float* g_ent, float* dh, float* dW, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   int rc = check_shape(N, H, V, chunk_size);
+  if (rc != LMH_OK) return rc;
+  rc = check_temperature(temperature);
   if (rc != LMH_OK) return rc;
   if (g_ent != nullptr && entropy == nullptr)
     return fail(LMH_ERR_ARGS, "bwd: g_ent given without the forward's entropy");
@@ -227,6 +249,8 @@ int lmhead_logps_bwd(const uint16_t* hidden, const uint16_t* W, const int32_t* t
   st.entropy = entropy;
   st.g_logp = g_logp;
   st.g_ent = g_ent;
+  st.sc = temper_scale(temperature);
+  st.invT = inv_temperature(temperature);
   st.ht = ht;
   st.ld_ht = p.N_pad;
   st.Wt = Wt;
@@ -272,6 +296,21 @@ int lmhead_logps_bwd(const uint16_t* hidden, const uint16_t* W, const int32_t* t
     if (e != hipSuccess) return fail(LMH_ERR_HIP, "bwd: launch failed: %s", hipGetErrorString(e));
   }
   return ok();
+}
+
+int lmhead_logps_fwd(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, int64_t N,
+                     int64_t H, int64_t V, int64_t chunk_size, float* logp, float* entropy,
+                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return lmhead_logps_fwd_temp(hidden, W, targets, N, H, V, chunk_size, 1.0f, logp, entropy, lse,
+                               workspace, workspace_bytes, stream);
+}
+
+int lmhead_logps_bwd(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, int64_t N,
+                     int64_t H, int64_t V, int64_t chunk_size, const float* lse,
+                     const float* entropy, const float* g_logp, const float* g_ent, float* dh,
+                     float* dW, void* workspace, size_t workspace_bytes, void* stream) {
+  return lmhead_logps_bwd_temp(hidden, W, targets, N, H, V, chunk_size, 1.0f, lse, entropy, g_logp,
+                               g_ent, dh, dW, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

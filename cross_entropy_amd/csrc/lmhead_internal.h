@@ -41,6 +41,8 @@ struct FwdArgs {
   const int32_t* targets;
   int64_t N, H, V;
   int S, n_tt, n_vt;
+  float sc;     // log2(e) / T
+  float invT;   // 1 / T
   void* part;
   int64_t part_ld;
   float* logp;
@@ -59,6 +61,8 @@ struct BwdStep {
   const float* entropy;
   const float* g_logp;
   const float* g_ent;
+  float sc;     // log2(e) / T
+  float invT;   // 1 / T
   const uint16_t* ht;   // hidden^T [H_pad][N_pad], masked tokens zeroed
   int64_t ld_ht;
   const uint16_t* Wt;   // W^T [H_pad][V_pad]

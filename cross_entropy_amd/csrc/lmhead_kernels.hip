@@ -370,9 +370,11 @@ __device__ __forceinline__ Stats merge_stats(Stats a, Stats b) {
 // Forward tile kernel. Workgroup (token tile tt, split s) walks vocabulary
 // tiles s, s + S, s + 2S, ... for its 256 tokens (A = W rows = vocabulary,
 // B = hidden rows = tokens) and writes one partial Stats per token and split.
+// sc = log2(e) / T scores the tempered logits z / T in base 2; the target
+// logit is kept untempered (the merge scales it).
 __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W,
-    const int32_t* __restrict__ targets, int N, int H, int V, int S, int n_tt, int n_vt,
+    const int32_t* __restrict__ targets, int N, int H, int V, int S, int n_tt, int n_vt, float sc,
     float4* __restrict__ part, int64_t part_ld) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const int vid = xcd_remap(blockIdx.x, gridDim.x);
@@ -412,7 +414,12 @@ __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
     }
 
     const int vrow0 = v0 + wm * 128;
-    if (vrow0 + 128 > V) {   // ragged last tile: rows past V take no part
+    // ragged last tile: rows past V take no part. Their logits are set to
+    // kNegBig so they never win the max (unless the wave has no row left),
+    // and their exponentials are zeroed outright: scaled by sc < 1 the
+    // rounding error of kNegBig * sc alone would overflow exp2.
+    const bool ragged = vrow0 + 128 > V;
+    if (ragged) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -440,20 +447,33 @@ __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
-      const float mnew = fmaxf(st[j].m2, mx * kLog2e);
+      const float mnew = fmaxf(st[j].m2, mx * sc);   // sc > 0: max commutes with the scaling
       const float dm = st[j].m2 - mnew;
       const float alpha = fast_exp2(dm);
       float s1 = alpha * st[j].s1;
       float s2 = alpha * (st[j].s2 + dm * st[j].s1);
+      if (!ragged) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float d = fmaf(acc[i][j][r], kLog2e, -mnew);
-          const float e = fast_exp2(d);
-          s1 += e;
-          s2 = fmaf(e, d, s2);
-        }
+          for (int r = 0; r < 16; ++r) {
+            const float d = fmaf(acc[i][j][r], sc, -mnew);
+            const float e = fast_exp2(d);
+            s1 += e;
+            s2 = fmaf(e, d, s2);
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool live = vrow0 + acc_row(i, r, lane) < V;
+            const float d = live ? fmaf(acc[i][j][r], sc, -mnew) : 0.0f;
+            const float e = live ? fast_exp2(d) : 0.0f;
+            s1 += e;
+            s2 = fmaf(e, d, s2);
+          }
+      }
       st[j].m2 = mnew;
       st[j].s1 = s1;
       st[j].s2 = s2;
@@ -491,9 +511,11 @@ __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
 }
 
 // Split merge: per token, the S partials in split order, by log-sum-exp.
+// invT = 1 / T tempers the target logit.
 __global__ __launch_bounds__(256) void fwd_merge_kernel(
     const float4* __restrict__ part, int64_t part_ld, int S, const int32_t* __restrict__ targets,
-    int N, int V, float* __restrict__ logp, float* __restrict__ entropy, float* __restrict__ lse) {
+    int N, int V, float invT, float* __restrict__ logp, float* __restrict__ entropy,
+    float* __restrict__ lse) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= N) return;
   float4 q = part[i];
@@ -507,7 +529,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(
   const float l2s = log2f(a.s1);
   const float l = kLn2 * (a.m2 + l2s);               // lse = m + ln(sum e^(z-m))
   const float h = kLn2 * (l2s - a.s2 / a.s1);        // lse - sum p z
-  logp[i] = valid ? a.zt - l : 0.0f;
+  logp[i] = valid ? a.zt * invT - l : 0.0f;
   lse[i] = valid ? l : 0.0f;
   if (entropy != nullptr) entropy[i] = valid ? h : 0.0f;
 }
@@ -522,8 +544,9 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(
 // and stream order makes every buffer's writes precede its reads.
 
 // Cotangent tile: recompute a 256 x 256 logits tile of block
-// [t0, t0 + Ct) x [v0, v0 + Vb) and write
-//   dz = g_l (onehot - p) - g_e p (log p + entropy),  p = 2^(z log2e - lse log2e)
+// [t0, t0 + Ct) x [v0, v0 + Vb) and write the untempered logits' cotangent
+//   dz = (g_l (onehot - p) - g_e p (log p + entropy)) / T,
+//   p = 2^(z sc - lse log2e),  sc = log2(e) / T,
 // as bf16. Tokens past the block, masked tokens and vocabulary past the block
 // are written as 0, so the gradient GEMMs can run over the padded block.
 __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
@@ -559,9 +582,10 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
     const float ga = (live[j] && s.g_logp != nullptr) ? s.g_logp[tok] : 0.0f;
     const float gb = (live[j] && s.g_ent != nullptr) ? s.g_ent[tok] : 0.0f;
     nlseL[j] = -L * kLog2e;
-    c0[j] = -(ga + gb * Hn);     // dz = p * (c1 * d + c0) (+ g_l at the target), d = log2 p
-    c1[j] = -(gb * kLn2);
-    gl[j] = ga;
+    // dz = p * (c1 * d + c0) (+ g_l / T at the target), d = log2 p
+    c0[j] = -(ga + gb * Hn) * s.invT;
+    c1[j] = -(gb * kLn2) * s.invT;
+    gl[j] = ga * s.invT;
     tr[j] = live[j] ? (t - v0 - vw0) : -1;
   }
   const bool any_dead = __any(!live[0] || !live[1]);
@@ -580,7 +604,7 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = g * 4 + q;
-          const float d = fmaf(acc[i][j][r], kLog2e, nlseL[j]);
+          const float d = fmaf(acc[i][j][r], s.sc, nlseL[j]);
           const float p = fast_exp2(d);
           float x = p * fmaf(c1[j], d, c0[j]);
           if (hit_any) x = (acc_row(i, r, lane) == tr[j]) ? x + gl[j] : x;
@@ -760,7 +784,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   const double N = (double)a.N, H = (double)a.H, V = (double)a.V;
   trace_begin(stream);
   hipLaunchKernelGGL(fwd_stats_kernel, dim3(round8(wg)), dim3(kThreads), 0, stream, a.hidden, a.W,
-                     a.targets, (int)a.N, (int)a.H, (int)a.V, a.S, a.n_tt, a.n_vt,
+                     a.targets, (int)a.N, (int)a.H, (int)a.V, a.S, a.n_tt, a.n_vt, a.sc,
                      reinterpret_cast<float4*>(a.part), a.part_ld);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -768,7 +792,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   trace_begin(stream);
   hipLaunchKernelGGL(fwd_merge_kernel, dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, stream,
                      reinterpret_cast<const float4*>(a.part), a.part_ld, a.S, a.targets, (int)a.N,
-                     (int)a.V, a.logp, a.entropy, a.lse);
+                     (int)a.V, a.invT, a.logp, a.entropy, a.lse);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   trace_end(kFwdMerge, stream, 0.0, 16.0 * a.S * N + 16.0 * N);

@@ -75,7 +75,7 @@ extern "C" {
 #define LMH_ERR_SHAPE (-2)       /* N < 0, H <= 0, V <= 0 or V >= 2^31 */
 #define LMH_ERR_CHUNK (-3)       /* chunk_size <= 0 */
 #define LMH_ERR_WORKSPACE (-4)   /* workspace smaller than the queried size */
-#define LMH_ERR_ARGS (-5)        /* g_ent given without entropy */
+#define LMH_ERR_ARGS (-5)        /* g_ent given without entropy; bad temperature */
 #define LMH_ERR_UNSUPPORTED (-6) /* H % 64 != 0, or a misaligned pointer */
 #define LMH_ERR_HIP (-7)         /* a HIP call or kernel launch failed */
 
@@ -133,6 +133,29 @@ int lmhead_logps_bwd(const uint16_t* hidden, const uint16_t* W, const int32_t* t
                      const float* g_logp, const float* g_ent,
                      float* dh, float* dW,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Tempered head (google/tunix pull request #2913 runs its head at
+ * temperatures 1 and 0.7): the same two calls scoring the tempered logits
+ * z / T. logp, entropy and lse are those of softmax(z / T) (lse of z / T);
+ * the backward's cotangent of the tempered logits is divided by T before
+ * both gradient matmuls, so dh and dW are gradients with respect to the
+ * untempered hidden and W. The backward needs the tempered forward's lse and
+ * entropy and the same T. temperature must be finite and > 0 with 1 / T
+ * finite in float32, otherwise LMH_ERR_ARGS; all other arguments, layouts, ownership and errors are those
+ * of lmhead_logps_fwd / lmhead_logps_bwd, which are these calls at T = 1
+ * (bit for bit).
+ */
+int lmhead_logps_fwd_temp(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
+                          int64_t N, int64_t H, int64_t V, int64_t chunk_size, float temperature,
+                          float* logp, float* entropy, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+int lmhead_logps_bwd_temp(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
+                          int64_t N, int64_t H, int64_t V, int64_t chunk_size, float temperature,
+                          const float* lse, const float* entropy,
+                          const float* g_logp, const float* g_ent,
+                          float* dh, float* dW,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Thread-local message of the calling thread's last failing call ("" if none). */
 const char* lmhead_logps_last_error(void);

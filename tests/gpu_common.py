@@ -29,18 +29,21 @@ def dev(a: np.ndarray):
 
 
 def run_head(h_bits, W_bits, targets, chunk_size, g_l=None, g_e=None, with_entropy=True, backward=True,
-             entropy_grad=True):
-    """Forward (and backward) on the GPU; returns numpy arrays."""
+             entropy_grad=True, temperature=None):
+    """Forward (and backward) on the GPU; returns numpy arrays. ``temperature``
+    None runs the plain entry points, a number the tempered ones."""
     import torch
     import cross_entropy_amd as lm
     h, W, t = dev_bits(h_bits), dev_bits(W_bits), dev(targets.astype(np.int32))
     ws = lm.workspace_for(h, W, chunk_size, with_backward=True)
-    logp, ent, lse = lm.forward(h, W, t, chunk_size, with_entropy=with_entropy, workspace=ws)
+    logp, ent, lse = lm.forward(h, W, t, chunk_size, with_entropy=with_entropy, workspace=ws,
+                                temperature=temperature)
     out = {"logp": logp, "entropy": ent, "lse": lse}
     if backward:
         gl = None if g_l is None else dev(np.asarray(g_l, dtype=np.float32))
         ge = None if (g_e is None or not entropy_grad) else dev(np.asarray(g_e, dtype=np.float32))
-        dh, dW = lm.backward(h, W, t, chunk_size, lse, ent if ge is not None else None, gl, ge, workspace=ws)
+        dh, dW = lm.backward(h, W, t, chunk_size, lse, ent if ge is not None else None, gl, ge, workspace=ws,
+                             temperature=temperature)
         out["dh"], out["dW"] = dh, dW
     torch.cuda.synchronize()
     return {k: (None if v is None else v.cpu().numpy()) for k, v in out.items()}

@@ -87,6 +87,34 @@ def test_backward_null_args_alignment_and_workspace_errors():
     assert _bwd(workspace_bytes=need - 1) == -4
 
 
+def _fwd_t(temperature, **kw):
+    a = dict(hidden=FAKE, W=FAKE, targets=FAKE, N=64, H=128, V=300, chunk_size=16, temperature=temperature,
+             logp=FAKE, entropy=FAKE, lse=FAKE, workspace=FAKE, workspace_bytes=0, stream=0)
+    a.update(kw)
+    return nat.raw_fwd_temp(**a)
+
+
+def _bwd_t(temperature, **kw):
+    a = dict(hidden=FAKE, W=FAKE, targets=FAKE, N=64, H=128, V=300, chunk_size=16, temperature=temperature,
+             lse=FAKE, entropy=FAKE, g_logp=FAKE, g_ent=FAKE, dh=FAKE, dW=FAKE, workspace=FAKE,
+             workspace_bytes=0, stream=0)
+    a.update(kw)
+    return nat.raw_bwd_temp(**a)
+
+
+@pytest.mark.parametrize("call", [_fwd_t, _bwd_t])
+def test_temperature_errors(call):
+    """The tempered calls reject a temperature that is not finite and > 0
+    (LMH_ERR_ARGS) and otherwise check arguments like the plain calls."""
+    for bad in (0.0, -0.7, float("nan"), float("inf"), -float("inf"), 1e-40):
+        assert call(bad) == -5, bad
+        assert "temperature" in nat.load().lmhead_logps_last_error().decode()
+    assert call(0.7, N=-1) == -2
+    assert call(0.7, chunk_size=0) == -3
+    assert call(0.7, H=96) == -6
+    assert call(0.7, workspace_bytes=0) == -4        # valid temperature: fails on the workspace next
+
+
 def test_workspace_query_errors():
     import ctypes
     assert nat.load().lmhead_logps_workspace_bytes(1, 64, 10, 4, 0, None) == -1
