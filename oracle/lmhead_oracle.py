@@ -43,6 +43,21 @@ through z / T).
    differentiates the entropy adds the entropy term; both gradient matmuls
    read that one cotangent.]
 
+Non-finite logits (unmasked rows; they arise only from non-finite W or
+hidden values). tunix #2913 checks its fused scoring against the textbook
+log-softmax and entropy on logits with inf, -inf and NaN entries and on a row
+of no finite logit. The reading taken here is IEEE evaluation of the
+definitions above, with the log-sum-exp shifted by the row max when that max
+is finite and by 0 otherwise:
+  * -inf entries have exp = 0 and drop out of lse; a -inf target gives
+    logp = -inf; the entropy's p * (z - lse) is 0 * -inf = NaN;
+  * a +inf entry (and no NaN) gives lse = +inf, logp = -inf for a finite
+    target and NaN for a +inf target, entropy NaN;
+  * a NaN entry makes lse, logp and entropy NaN;
+  * a row of no finite logit (all -inf) has lse = -inf, logp = entropy = NaN.
+Gradients follow the same IEEE arithmetic (non-finite inputs generally make
+them NaN); masked rows stay exactly 0.
+
 Readings taken where the pages leave a step open: chunk_size counts flattened
 tokens, the last chunk may be partial (tunix #2913 tests "chunks that do not
 divide the local sequence and one chunk for all of it"); masked lse is 0;
@@ -109,14 +124,18 @@ def _raw_cotangent(dz: np.ndarray, temperature: float) -> np.ndarray:
 
 
 def _log_sum_exp(z: np.ndarray) -> np.ndarray:
-    """Step 3: lse = m + log(sum exp(z - m)) per row."""
+    """Step 3: lse = m + log(sum exp(z - m)) per row, m the row max when it is
+    finite and 0 otherwise (a row holding +inf, NaN or only -inf)."""
     m = np.max(z, axis=1, keepdims=True)
-    return (m + np.log(np.sum(np.exp(z - m), axis=1, keepdims=True)))[:, 0]
+    m = np.where(np.isfinite(m), m, 0.0)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        return (m + np.log(np.sum(np.exp(z - m), axis=1, keepdims=True)))[:, 0]
 
 
 def _probs(z: np.ndarray, lse: np.ndarray) -> np.ndarray:
     """p = exp(z - lse) per row."""
-    return np.exp(z - lse[:, None])
+    with np.errstate(invalid="ignore", over="ignore"):
+        return np.exp(z - lse[:, None])
 
 
 def _target_logit(z: np.ndarray, t: np.ndarray) -> np.ndarray:
@@ -126,12 +145,14 @@ def _target_logit(z: np.ndarray, t: np.ndarray) -> np.ndarray:
 
 def _entropy(z: np.ndarray, lse: np.ndarray, p: np.ndarray) -> np.ndarray:
     """Step 4: entropy = -sum_v p_v log p_v with log p = z - lse."""
-    return -np.sum(p * (z - lse[:, None]), axis=1)
+    with np.errstate(invalid="ignore"):
+        return -np.sum(p * (z - lse[:, None]), axis=1)
 
 
 def _cotangent(z, lse, p, ent, t, g_l, g_e) -> np.ndarray:
     """Step 5: dz = g_l (onehot(t) - p) - g_e p (log p + entropy)."""
-    dz = -g_l[:, None] * p - g_e[:, None] * p * ((z - lse[:, None]) + ent[:, None])
+    with np.errstate(invalid="ignore"):
+        dz = -g_l[:, None] * p - g_e[:, None] * p * ((z - lse[:, None]) + ent[:, None])
     dz[np.arange(z.shape[0]), t] += g_l
     return dz
 
@@ -144,10 +165,12 @@ def _check_temperature(temperature):
 
 
 def _rows_stats(h_rows, W, t, temperature=1.0):
-    z = _temper(_logits(h_rows, W), temperature)
+    with np.errstate(invalid="ignore", over="ignore"):
+        z = _temper(_logits(h_rows, W), temperature)
     lse = _log_sum_exp(z)
     p = _probs(z, lse)
-    logp = _target_logit(z, t) - lse
+    with np.errstate(invalid="ignore"):
+        logp = _target_logit(z, t) - lse
     ent = _entropy(z, lse, p)
     return z, lse, p, logp, ent
 
@@ -226,8 +249,9 @@ def backward(hidden_bits, W_bits, targets, chunk_size: int, g_logp=None, g_ent=N
             z, l, p, _, en = _rows_stats(h[rows], W, t[rows], T)
             dz = _raw_cotangent(_cotangent(z, l, p, en, t[rows], g_l[rows], g_e[rows]), T)
             out = rows if pos is None else np.array([pos[int(i)] for i in rows], dtype=np.int64)
-            dh[out] = dz @ W
-            dW += dz.T @ h[rows]
+            with np.errstate(invalid="ignore", over="ignore"):
+                dh[out] = dz @ W
+                dW += dz.T @ h[rows]
     return dh, dW
 
 

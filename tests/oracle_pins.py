@@ -357,6 +357,87 @@ def pin_temperature_limit():
     _close(r["dh"], ref_dh, 1e-6, 1e-20, what="T->inf dh")
 
 
+# --- non-finite logits (unmasked rows) ---------------------------------------------
+# tunix #2913 checks its fused scoring against the textbook log-softmax and
+# entropy on logits with inf, -inf and NaN entries and a row of no finite
+# logit. Reading: IEEE evaluation of the definitions, the log-sum-exp shifted
+# by the row max when it is finite and by 0 otherwise.
+
+_BF16_POS_INF, _BF16_NEG_INF, _BF16_NAN = 0x7F80, 0xFF80, 0x7FC0
+
+
+def _special_case(seed=21, N=6, H=5, V=9):
+    rng = np.random.default_rng(seed)
+    h = bf16(np.abs(rng.standard_normal((N, H))) + 0.25)    # h[:, 0] > 0: inf * h0 keeps its sign
+    W = bf16(rng.standard_normal((V, H)) * 0.5)
+    t = rng.integers(0, V, size=N).astype(np.int32)
+    return h, W, t
+
+
+def _row_only(W, v, first):
+    W = W.copy()
+    W[v] = 0
+    W[v, 0] = first
+    return W
+
+
+def pin_nonfinite_logits():
+    """Closed forms of the non-finite cases: a -inf entry drops out (equal to
+    the row without that vocabulary entry) and makes the entropy NaN; a -inf
+    target gives logp = -inf; +inf gives lse = +inf and logp = -inf (NaN at a
+    +inf target); NaN makes everything NaN; a row of no finite logit has
+    lse = -inf and NaN logp and entropy. Masked tokens stay exactly 0."""
+    h, W, t = _special_case()
+    N, V = h.shape[0], W.shape[0]
+    v = 4
+    t[:] = np.where(t == v, 0, t)
+    t[1] = v                       # token 1 targets the special row
+    t[5] = -1                      # token 5 is masked
+
+    def run(Wb, tb=t, hb=h):
+        return O.forward(hb, Wb, tb, 4)
+
+    keep = np.array([i for i in range(V) if i != v])
+    t_red = np.where(t > v, t - 1, t)
+
+    # -inf entry: drops out of lse; -inf target -> logp -inf; entropy NaN
+    lp, en, ls = run(_row_only(W, v, _BF16_NEG_INF))
+    rlp, ren, rls = O.forward(h, W[keep], np.where(t == v, 0, t_red), 4)
+    others = np.array([0, 2, 3, 4])
+    _close(ls[others], rls[others], 1e-14, 1e-15, what="-inf entry: lse without it")
+    _close(lp[others], rlp[others], 1e-14, 1e-15, what="-inf entry: logp without it")
+    _close(ls[1], rls[1], 1e-14, 1e-15, what="-inf target: lse without it")
+    assert lp[1] == -np.inf, "a -inf target logit gives logp = -inf"
+    assert np.all(np.isnan(en[[0, 1, 2, 3, 4]])), "entropy of a row with a -inf entry is NaN (0 * -inf)"
+    assert lp[5] == en[5] == ls[5] == 0.0
+
+    # +inf entry: lse = +inf, logp = -inf (finite target) / NaN (the +inf target), entropy NaN
+    lp, en, ls = run(_row_only(W, v, _BF16_POS_INF))
+    assert np.all(ls[[0, 1, 2, 3, 4]] == np.inf), "+inf entry: lse = +inf"
+    assert np.all(lp[others] == -np.inf) and np.isnan(lp[1]), "+inf entry: logp = -inf, NaN at the target"
+    assert np.all(np.isnan(en[[0, 1, 2, 3, 4]]))
+    assert lp[5] == en[5] == ls[5] == 0.0
+
+    # NaN entry: everything NaN
+    lp, en, ls = run(_row_only(W, v, _BF16_NAN))
+    for name, a in (("logp", lp), ("entropy", en), ("lse", ls)):
+        assert np.all(np.isnan(a[[0, 1, 2, 3, 4]])), f"NaN entry: {name} NaN"
+        assert a[5] == 0.0
+
+    # a row of no finite logit: token 2's hidden is [+inf, 0, ...] and W[:, 0] < 0
+    W2 = W.copy()
+    W2[:, 0] = bf16(-(np.abs(f64(W[:, 0])) + 0.125))
+    h2 = h.copy()
+    h2[2] = 0
+    h2[2, 0] = _BF16_POS_INF
+    lp, en, ls = run(W2, hb=h2)
+    assert ls[2] == -np.inf and np.isnan(lp[2]) and np.isnan(en[2]), "no finite logit: lse -inf, NaN logp/entropy"
+    rlp, ren, rls = run(W2)
+    fine = np.array([0, 1, 3, 4])
+    for a, r, name in ((lp, rlp, "logp"), (en, ren, "entropy"), (ls, rls, "lse")):
+        _close(a[fine], r[fine], 0.0, 0.0, what=f"other tokens unaffected ({name})")
+
+
 ALL_PINS = [
     pin_W_zero,
     pin_h_zero,
@@ -374,4 +455,5 @@ ALL_PINS = [
     pin_temperature_bruteforce,
     pin_temperature_fd,
     pin_temperature_limit,
+    pin_nonfinite_logits,
 ]

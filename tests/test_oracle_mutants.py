@@ -95,6 +95,17 @@ def _m_backward_temperature_division_dropped(dz, temperature):
     return dz
 
 
+def _m_lse_shift_always_max(z):
+    m = np.max(z, axis=1, keepdims=True)
+    with np.errstate(invalid="ignore", divide="ignore", over="ignore"):
+        return (m + np.log(np.sum(np.exp(z - m), axis=1, keepdims=True)))[:, 0]
+
+
+def _m_entropy_zero_times_log_zero(z, lse, p):
+    with np.errstate(invalid="ignore"):
+        return -np.sum(np.where(p > 0, p * (z - lse[:, None]), 0.0), axis=1)
+
+
 _orig = {}
 
 MUTANTS = {
@@ -115,6 +126,8 @@ MUTANTS = {
     "temperature_ignored": ("_temper", _m_temperature_ignored),
     "temperature_multiplied": ("_temper", _m_temperature_multiplied),
     "backward_temperature_division_dropped": ("_raw_cotangent", _m_backward_temperature_division_dropped),
+    "lse_shift_by_nonfinite_max": ("_log_sum_exp", _m_lse_shift_always_max),
+    "entropy_zero_log_zero_convention": ("_entropy", _m_entropy_zero_times_log_zero),
 }
 
 
