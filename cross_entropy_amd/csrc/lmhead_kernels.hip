@@ -57,6 +57,10 @@ constexpr float kNegBig = -1.0e30f;              // "minus infinity" that keeps 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// NaN-propagating max (v_maximum3_f32 on gfx950): a NaN logit must reach the
+// statistics, where fmaxf would drop it.
+__device__ __forceinline__ float nan_max(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v = {lo, hi};
   bf16x2 b = __builtin_convertvector(v, bf16x2);   // round to nearest even
@@ -353,7 +357,7 @@ struct Stats {
 };
 
 __device__ __forceinline__ Stats merge_stats(Stats a, Stats b) {
-  const float m = fmaxf(a.m2, b.m2);
+  const float m = nan_max(a.m2, b.m2);
   const float da = a.m2 - m;
   const float db = b.m2 - m;
   const float ea = fast_exp2(da);
@@ -446,8 +450,8 @@ __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
-      const float mnew = fmaxf(st[j].m2, mx * sc);   // sc > 0: max commutes with the scaling
+        for (int r = 0; r < 16; ++r) mx = nan_max(mx, acc[i][j][r]);
+      const float mnew = nan_max(st[j].m2, mx * sc);   // sc > 0: max commutes with the scaling
       const float dm = st[j].m2 - mnew;
       const float alpha = fast_exp2(dm);
       float s1 = alpha * st[j].s1;
@@ -527,7 +531,9 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(
   const int t = targets[i];
   const bool valid = (t >= 0) && (t < V);
   const float l2s = log2f(a.s1);
-  const float l = kLn2 * (a.m2 + l2s);               // lse = m + ln(sum e^(z-m))
+  // lse = m + ln(sum e^(z-m)); a +inf logit (and no NaN) leaves m = +inf and
+  // s1 = NaN (inf - inf): the log-sum-exp is +inf
+  const float l = a.m2 == INFINITY ? INFINITY : kLn2 * (a.m2 + l2s);
   const float h = kLn2 * (l2s - a.s2 / a.s1);        // lse - sum p z
   logp[i] = valid ? a.zt * invT - l : 0.0f;
   lse[i] = valid ? l : 0.0f;

@@ -55,6 +55,18 @@
  *    on distinct streams may be used from several threads at once (the
  *    optional tracing at the end of this header is the one exception).
  *  - Outputs are overwritten in full (dW is not accumulated into).
+ *  - Non-finite logits in unmasked rows (they arise only from non-finite W
+ *    or hidden values; tunix #2913 checks its scoring on inf, -inf and NaN
+ *    logits and on a row of no finite logit) follow IEEE evaluation of the
+ *    definitions above, the log-sum-exp shifted by the row max when that max
+ *    is finite and by 0 otherwise: a -inf entry drops out of lse and a -inf
+ *    target gives logp = -inf, while the entropy's p (z - lse) = 0 * -inf
+ *    makes that row's entropy NaN; a +inf entry (and no NaN) gives
+ *    lse = +inf, logp = -inf (NaN when the target is the +inf entry) and a
+ *    NaN entropy; any NaN entry makes the row's three values NaN; a row of
+ *    no finite logit has lse = -inf and NaN logp and entropy. Gradients
+ *    follow the same arithmetic, so non-finite inputs generally make dh and
+ *    dW NaN. Masked rows are 0 whatever their hidden row holds.
  *  - Return value: LMH_OK (0) or a negative LMH_ERR_* code. Argument checks
  *    run on the host before anything is enqueued, so a failing call enqueues
  *    nothing. lmhead_logps_last_error() gives a thread-local message for the
