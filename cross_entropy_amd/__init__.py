@@ -14,8 +14,11 @@ Entry points mirror the C ABI:
                      dh, dW, workspace)
     lmhead_logps_fwd_temp / lmhead_logps_bwd_temp   (the same with a temperature
                      after chunk_size: the head scores the logits divided by it)
-and two allocating helpers, ``forward`` and ``backward`` (``temperature=``
-selects the tempered calls).
+    lmhead_logps_bwd_ex  (tempered backward that can add into dh / dW)
+two allocating helpers, ``forward`` and ``backward`` (``temperature=``
+selects the tempered calls, ``dh=`` / ``dW=`` with ``accumulate=`` add into
+caller buffers), and ``lmhead_logps``, a ``torch.autograd.Function`` front
+end for training code.
 """
 from __future__ import annotations
 
@@ -31,6 +34,8 @@ __all__ = [
     "lmhead_logps_bwd",
     "lmhead_logps_fwd_temp",
     "lmhead_logps_bwd_temp",
+    "lmhead_logps_bwd_ex",
+    "lmhead_logps",
     "forward",
     "backward",
     "version",
@@ -166,6 +171,14 @@ def lmhead_logps_bwd_temp(hidden, W, targets, chunk_size: int, temperature: floa
     _native.check(_native.raw_bwd_temp(*ptrs, temperature, *rest))
 
 
+def lmhead_logps_bwd_ex(hidden, W, targets, chunk_size: int, temperature: float, lse, entropy, g_logp, g_ent,
+                        dh, dW, flags: int, workspace, stream=None) -> None:
+    """Enqueue the backward with flags (``_native.BWD_ACCUMULATE_DH`` /
+    ``BWD_ACCUMULATE_DW``: add into dh / dW instead of overwriting)."""
+    ptrs, rest = _bwd_args(hidden, W, targets, chunk_size, lse, entropy, g_logp, g_ent, dh, dW, workspace, stream)
+    _native.check(_native.raw_bwd_ex(*ptrs, temperature, *rest[:6], flags, *rest[6:]))
+
+
 def workspace_for(hidden, W, chunk_size: int, with_backward: bool = True):
     torch = _torch()
     N, H = hidden.shape
@@ -194,20 +207,84 @@ def forward(hidden, W, targets, chunk_size: int, with_entropy: bool = True, work
 
 
 def backward(hidden, W, targets, chunk_size: int, lse, entropy, g_logp, g_ent: Optional = None,
-             workspace=None, stream=None, temperature: Optional[float] = None) -> Tuple:
-    """Allocate gradients (torch) and run the backward: (dh, dW), float32.
-    ``temperature`` must match the forward that produced lse and entropy."""
+             workspace=None, stream=None, temperature: Optional[float] = None, dh=None, dW=None,
+             accumulate: bool = False) -> Tuple:
+    """Run the backward: (dh, dW), float32. Gradients are allocated unless
+    ``dh`` / ``dW`` are given; with ``accumulate`` the given buffers are
+    added into. ``temperature`` must match the forward that produced lse and
+    entropy."""
     torch = _torch()
     N, H = hidden.shape
     V = W.shape[0]
     dev = hidden.device
-    dh = torch.empty((N, H), dtype=torch.float32, device=dev)
-    dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+    if accumulate and (dh is None or dW is None):
+        raise ValueError("accumulate needs both dh and dW buffers")
+    if dh is None:
+        dh = torch.empty((N, H), dtype=torch.float32, device=dev)
+    if dW is None:
+        dW = torch.empty((V, H), dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = workspace_for(hidden, W, chunk_size, with_backward=True)
-    if temperature is None:
+    if accumulate:
+        flags = _native.BWD_ACCUMULATE_DH | _native.BWD_ACCUMULATE_DW
+        lmhead_logps_bwd_ex(hidden, W, targets, chunk_size, 1.0 if temperature is None else temperature, lse,
+                            entropy, g_logp, g_ent, dh, dW, flags, workspace, stream)
+    elif temperature is None:
         lmhead_logps_bwd(hidden, W, targets, chunk_size, lse, entropy, g_logp, g_ent, dh, dW, workspace, stream)
     else:
         lmhead_logps_bwd_temp(hidden, W, targets, chunk_size, temperature, lse, entropy, g_logp, g_ent, dh, dW,
                               workspace, stream)
     return dh, dW
+
+
+def _autograd_function():
+    torch = _torch()
+
+    class _LmheadLogps(torch.autograd.Function):
+        """logp (and entropy) of the head with its backward through the
+        library; gradients come back in the inputs' dtypes."""
+
+        @staticmethod
+        def forward(ctx, hidden, W, targets, chunk_size, temperature, with_entropy):
+            ws = workspace_for(hidden, W, chunk_size, with_backward=True)
+            logp, ent, lse = forward(hidden, W, targets, chunk_size, with_entropy=with_entropy, workspace=ws,
+                                     temperature=temperature)
+            ctx.chunk_size = chunk_size
+            ctx.temperature = temperature
+            ctx.with_entropy = with_entropy
+            ctx.workspace = ws
+            saved = (hidden, W, targets, lse) + ((ent,) if with_entropy else ())
+            ctx.save_for_backward(*saved)
+            if with_entropy:
+                return logp, ent
+            return logp
+
+        @staticmethod
+        def backward(ctx, g_logp, g_ent=None):
+            hidden, W, targets, lse = ctx.saved_tensors[:4]
+            ent = ctx.saved_tensors[4] if ctx.with_entropy else None
+            gl = None if g_logp is None else g_logp.detach().contiguous().float()
+            ge = None if (g_ent is None or ent is None) else g_ent.detach().contiguous().float()
+            dh, dW = backward(hidden, W, targets, ctx.chunk_size, lse, ent if ge is not None else None, gl, ge,
+                              workspace=ctx.workspace, temperature=ctx.temperature)
+            ctx.workspace = None
+            return (dh.to(hidden.dtype) if ctx.needs_input_grad[0] else None,
+                    dW.to(W.dtype) if ctx.needs_input_grad[1] else None,
+                    None, None, None, None)
+
+    return _LmheadLogps
+
+
+_FN = None
+
+
+def lmhead_logps(hidden, W, targets, chunk_size: int, temperature: Optional[float] = None, with_entropy: bool = True):
+    """Differentiable head for training code: returns ``(logp, entropy)``
+    (or ``logp`` alone without entropy). ``hidden`` [N, H] and ``W`` [V, H]
+    are bfloat16 tensors on one GPU; a backward through either output runs
+    ``lmhead_logps_bwd`` on the saved lse / entropy (the logits are recomputed,
+    never stored). Masked targets (outside [0, V)) give zeros."""
+    global _FN
+    if _FN is None:
+        _FN = _autograd_function()
+    return _FN.apply(hidden, W, targets, chunk_size, temperature, with_entropy)

@@ -28,6 +28,7 @@ EXPORTED = (
     "lmhead_logps_bwd",
     "lmhead_logps_fwd_temp",
     "lmhead_logps_bwd_temp",
+    "lmhead_logps_bwd_ex",
     "lmhead_logps_last_error",
     "lmhead_logps_version",
     "lmhead_logps_trace_enable",
@@ -87,6 +88,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lmhead_logps_fwd_temp.restype = ctypes.c_int
     lib.lmhead_logps_bwd_temp.argtypes = [p, p, p, i64, i64, i64, i64, f32, p, p, p, p, p, p, p, sz, p]
     lib.lmhead_logps_bwd_temp.restype = ctypes.c_int
+    lib.lmhead_logps_bwd_ex.argtypes = [p, p, p, i64, i64, i64, i64, f32, p, p, p, p, p, p, ctypes.c_uint, p, sz, p]
+    lib.lmhead_logps_bwd_ex.restype = ctypes.c_int
     lib.lmhead_logps_last_error.argtypes = []
     lib.lmhead_logps_last_error.restype = ctypes.c_char_p
     lib.lmhead_logps_version.argtypes = []
@@ -147,6 +150,19 @@ def raw_bwd_temp(hidden, W, targets, N, H, V, chunk_size, temperature, lse, entr
                                         int(chunk_size), float(temperature), lse or None, entropy or None,
                                         g_logp or None, g_ent or None, dh or None, dW or None,
                                         workspace or None, int(workspace_bytes), stream or None)
+
+
+BWD_ACCUMULATE_DH = 1
+BWD_ACCUMULATE_DW = 2
+
+
+def raw_bwd_ex(hidden, W, targets, N, H, V, chunk_size, temperature, lse, entropy, g_logp, g_ent, dh, dW, flags,
+               workspace, workspace_bytes, stream) -> int:
+    """Call lmhead_logps_bwd_ex with integer addresses (0 = NULL); returns the status."""
+    return load().lmhead_logps_bwd_ex(hidden or None, W or None, targets or None, int(N), int(H), int(V),
+                                      int(chunk_size), float(temperature), lse or None, entropy or None,
+                                      g_logp or None, g_ent or None, dh or None, dW or None, int(flags),
+                                      workspace or None, int(workspace_bytes), stream or None)
 
 
 TRACE_KERNELS = ("fwd_stats_kernel", "fwd_merge_kernel", "bwd_step_kernel", "transpose_kernel",

@@ -203,20 +203,25 @@ int lmhead_logps_fwd_temp(const uint16_t* hidden, const uint16_t* W, const int32
   return ok();
 }
 
-int lmhead_logps_bwd_temp(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
-                          int64_t N, int64_t H, int64_t V, int64_t chunk_size, float temperature,
-                          const float* lse, const float* entropy, const float* g_logp,
-                          const float* g_ent, float* dh, float* dW, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+int lmhead_logps_bwd_ex(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
+                        int64_t N, int64_t H, int64_t V, int64_t chunk_size, float temperature,
+                        const float* lse, const float* entropy, const float* g_logp,
+                        const float* g_ent, float* dh, float* dW, unsigned flags, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   int rc = check_shape(N, H, V, chunk_size);
   if (rc != LMH_OK) return rc;
   rc = check_temperature(temperature);
   if (rc != LMH_OK) return rc;
+  if (flags & ~(unsigned)(LMH_BWD_ACCUMULATE_DH | LMH_BWD_ACCUMULATE_DW))
+    return fail(LMH_ERR_ARGS, "bwd: unknown flags 0x%x", flags);
+  const bool acc_dh = (flags & LMH_BWD_ACCUMULATE_DH) != 0;
+  const bool acc_dW = (flags & LMH_BWD_ACCUMULATE_DW) != 0;
   if (g_ent != nullptr && entropy == nullptr)
     return fail(LMH_ERR_ARGS, "bwd: g_ent given without the forward's entropy");
   if (!dW) return fail(LMH_ERR_NULL, "bwd: dW must be non-NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (N == 0) {
+    if (acc_dW) return ok();   // nothing to add
     const hipError_t e = lmh::launch_fill_zero(dW, V * H, s);
     if (e != hipSuccess) return fail(LMH_ERR_HIP, "bwd: launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -271,8 +276,8 @@ int lmhead_logps_bwd_temp(const uint16_t* hidden, const uint16_t* W, const int32
       st.g_Ct = (int)std::min(p.Ct, N - tb * p.Ct);
       st.g_v0 = (int)(vb * p.Vb);
       st.g_Vb = (int)std::min(p.Vb, V - vb * p.Vb);
-      st.g_acc_dh = vb > 0;
-      st.g_acc_dW = tb > 0;
+      st.g_acc_dh = vb > 0 || acc_dh;
+      st.g_acc_dW = tb > 0 || acc_dW;
       st.n_dw = (int)(lmh::ceil_div(st.g_Vb, lmh::kTileRows) * st.n_ht);
       st.n_dh = (int)(lmh::ceil_div(st.g_Ct, lmh::kTileRows) * st.n_ht);
     } else {
@@ -305,12 +310,21 @@ int lmhead_logps_fwd(const uint16_t* hidden, const uint16_t* W, const int32_t* t
                                workspace, workspace_bytes, stream);
 }
 
+int lmhead_logps_bwd_temp(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
+                          int64_t N, int64_t H, int64_t V, int64_t chunk_size, float temperature,
+                          const float* lse, const float* entropy, const float* g_logp,
+                          const float* g_ent, float* dh, float* dW, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return lmhead_logps_bwd_ex(hidden, W, targets, N, H, V, chunk_size, temperature, lse, entropy,
+                             g_logp, g_ent, dh, dW, 0u, workspace, workspace_bytes, stream);
+}
+
 int lmhead_logps_bwd(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, int64_t N,
                      int64_t H, int64_t V, int64_t chunk_size, const float* lse,
                      const float* entropy, const float* g_logp, const float* g_ent, float* dh,
                      float* dW, void* workspace, size_t workspace_bytes, void* stream) {
-  return lmhead_logps_bwd_temp(hidden, W, targets, N, H, V, chunk_size, 1.0f, lse, entropy, g_logp,
-                               g_ent, dh, dW, workspace, workspace_bytes, stream);
+  return lmhead_logps_bwd_ex(hidden, W, targets, N, H, V, chunk_size, 1.0f, lse, entropy, g_logp,
+                             g_ent, dh, dW, 0u, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

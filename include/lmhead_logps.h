@@ -169,6 +169,30 @@ int lmhead_logps_bwd_temp(const uint16_t* hidden, const uint16_t* W, const int32
                           float* dh, float* dW,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward that adds into the caller's gradient buffers (a trainer's
+ * float32 weight-gradient and activation-gradient accumulators; tunix #2913
+ * hands the head's gradients to the trainer's own accumulation). The same
+ * computation as lmhead_logps_bwd_temp, with
+ *   flags & LMH_BWD_ACCUMULATE_DH: dh += gradient (masked rows unchanged)
+ *                                   instead of dh = gradient;
+ *   flags & LMH_BWD_ACCUMULATE_DW: dW += gradient instead of dW = gradient
+ *                                   (N = 0 then leaves dW unchanged).
+ * The added values are summed in the same fixed block order as the
+ * overwriting call, then added to the buffer's previous contents block by
+ * block: deterministic, equal to "previous + gradient" up to float32
+ * summation order. Unknown flag bits: LMH_ERR_ARGS. Everything else is that
+ * of lmhead_logps_bwd_temp (temperature 1 for the untempered head).
+ */
+#define LMH_BWD_ACCUMULATE_DH 1u
+#define LMH_BWD_ACCUMULATE_DW 2u
+int lmhead_logps_bwd_ex(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
+                        int64_t N, int64_t H, int64_t V, int64_t chunk_size, float temperature,
+                        const float* lse, const float* entropy,
+                        const float* g_logp, const float* g_ent,
+                        float* dh, float* dW, unsigned flags,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Thread-local message of the calling thread's last failing call ("" if none). */
 const char* lmhead_logps_last_error(void);
 

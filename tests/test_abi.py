@@ -115,6 +115,21 @@ def test_temperature_errors(call):
     assert call(0.7, workspace_bytes=0) == -4        # valid temperature: fails on the workspace next
 
 
+def test_backward_ex_flags():
+    """lmhead_logps_bwd_ex accepts only its two accumulate bits."""
+    a = dict(hidden=FAKE, W=FAKE, targets=FAKE, N=64, H=128, V=300, chunk_size=16, temperature=1.0,
+             lse=FAKE, entropy=FAKE, g_logp=FAKE, g_ent=FAKE, dh=FAKE, dW=FAKE, workspace=FAKE,
+             workspace_bytes=0, stream=0)
+    for bad in (4, 8, 0x80000000):
+        assert nat.raw_bwd_ex(flags=bad, **a) == -5, bad
+        assert "flags" in nat.load().lmhead_logps_last_error().decode()
+    for good in (0, 1, 2, 3):
+        assert nat.raw_bwd_ex(flags=good, **a) == -4, good   # valid flags: fails on the workspace next
+    assert nat.BWD_ACCUMULATE_DH == 1 and nat.BWD_ACCUMULATE_DW == 2
+    src = open(HEADER).read()
+    assert "#define LMH_BWD_ACCUMULATE_DH 1u" in src and "#define LMH_BWD_ACCUMULATE_DW 2u" in src
+
+
 def test_workspace_query_errors():
     import ctypes
     assert nat.load().lmhead_logps_workspace_bytes(1, 64, 10, 4, 0, None) == -1
