@@ -15,6 +15,8 @@ Entry points mirror the C ABI:
     lmhead_logps_fwd_temp / lmhead_logps_bwd_temp   (the same with a temperature
                      after chunk_size: the head scores the logits divided by it)
     lmhead_logps_bwd_ex  (tempered backward that can add into dh / dW)
+    lmhead_logps_fwd_shard / lmhead_logps_merge_shards / lmhead_logps_bwd_shard
+                         (the head over vocabulary shards, partials merged by log-sum-exp)
 two allocating helpers, ``forward`` and ``backward`` (``temperature=``
 selects the tempered calls, ``dh=`` / ``dW=`` with ``accumulate=`` add into
 caller buffers), and ``lmhead_logps``, a ``torch.autograd.Function`` front
@@ -35,6 +37,9 @@ __all__ = [
     "lmhead_logps_fwd_temp",
     "lmhead_logps_bwd_temp",
     "lmhead_logps_bwd_ex",
+    "lmhead_logps_fwd_shard",
+    "lmhead_logps_merge_shards",
+    "lmhead_logps_bwd_shard",
     "lmhead_logps",
     "forward",
     "backward",
@@ -177,6 +182,45 @@ def lmhead_logps_bwd_ex(hidden, W, targets, chunk_size: int, temperature: float,
     ``BWD_ACCUMULATE_DW``: add into dh / dW instead of overwriting)."""
     ptrs, rest = _bwd_args(hidden, W, targets, chunk_size, lse, entropy, g_logp, g_ent, dh, dW, workspace, stream)
     _native.check(_native.raw_bwd_ex(*ptrs, temperature, *rest[:6], flags, *rest[6:]))
+
+
+def lmhead_logps_fwd_shard(hidden, W_shard, targets, vocab_offset: int, V_total: int, chunk_size: int,
+                           temperature: float, partial, workspace, stream=None) -> None:
+    """Enqueue one vocabulary shard's forward: partial f32 [N, 4] records."""
+    torch = _torch()
+    N, H, V = _shapes(hidden, W_shard, targets)
+    dev = hidden.device
+    _native.check(_native.raw_fwd_shard(
+        _ptr(hidden, "hidden", _bf16_types(), dev), _ptr(W_shard, "W_shard", _bf16_types(), dev),
+        _ptr(targets, "targets", (torch.int32,), dev), N, H, V, vocab_offset, V_total, chunk_size, temperature,
+        _ptr(partial, "partial", (torch.float32,), dev, 4 * N), _ptr(workspace, "workspace", (torch.uint8,), dev),
+        workspace.numel(), _stream(dev, stream)))
+
+
+def lmhead_logps_merge_shards(partials, targets, V_total: int, temperature: float, logp, entropy, lse,
+                              stream=None) -> None:
+    """Merge shard records partials f32 [P, N, 4] (shard order) into logp / entropy / lse."""
+    torch = _torch()
+    if partials.dim() != 3 or partials.shape[2] != 4:
+        raise ValueError("partials must be [P, N, 4]")
+    P, N = int(partials.shape[0]), int(partials.shape[1])
+    dev = partials.device
+    _native.check(_native.raw_merge_shards(
+        _ptr(partials, "partials", (torch.float32,), dev), P, _ptr(targets, "targets", (torch.int32,), dev, N),
+        N, V_total, temperature, _ptr(logp, "logp", (torch.float32,), dev, N),
+        _ptr(entropy, "entropy", (torch.float32,), dev, N, optional=True), _ptr(lse, "lse", (torch.float32,), dev, N),
+        _stream(dev, stream)))
+
+
+def lmhead_logps_bwd_shard(hidden, W_shard, targets, vocab_offset: int, V_total: int, chunk_size: int,
+                           temperature: float, lse, entropy, g_logp, g_ent, dh, dW_shard, flags: int, workspace,
+                           stream=None) -> None:
+    """Enqueue one vocabulary shard's backward (dW_shard, and its part of dh)."""
+    ptrs, rest = _bwd_args(hidden, W_shard, targets, chunk_size, lse, entropy, g_logp, g_ent, dh, dW_shard,
+                           workspace, stream)
+    hid, Wp, tg, N, H, V, C = ptrs
+    _native.check(_native.raw_bwd_shard(hid, Wp, tg, N, H, V, vocab_offset, V_total, C, temperature, *rest[:6],
+                                        flags, *rest[6:]))
 
 
 def workspace_for(hidden, W, chunk_size: int, with_backward: bool = True):

@@ -29,6 +29,9 @@ EXPORTED = (
     "lmhead_logps_fwd_temp",
     "lmhead_logps_bwd_temp",
     "lmhead_logps_bwd_ex",
+    "lmhead_logps_fwd_shard",
+    "lmhead_logps_merge_shards",
+    "lmhead_logps_bwd_shard",
     "lmhead_logps_last_error",
     "lmhead_logps_version",
     "lmhead_logps_trace_enable",
@@ -90,6 +93,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lmhead_logps_bwd_temp.restype = ctypes.c_int
     lib.lmhead_logps_bwd_ex.argtypes = [p, p, p, i64, i64, i64, i64, f32, p, p, p, p, p, p, ctypes.c_uint, p, sz, p]
     lib.lmhead_logps_bwd_ex.restype = ctypes.c_int
+    lib.lmhead_logps_fwd_shard.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, f32, p, p, sz, p]
+    lib.lmhead_logps_fwd_shard.restype = ctypes.c_int
+    lib.lmhead_logps_merge_shards.argtypes = [p, i64, p, i64, i64, f32, p, p, p, p]
+    lib.lmhead_logps_merge_shards.restype = ctypes.c_int
+    lib.lmhead_logps_bwd_shard.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, f32, p, p, p, p, p, p,
+                                           ctypes.c_uint, p, sz, p]
+    lib.lmhead_logps_bwd_shard.restype = ctypes.c_int
     lib.lmhead_logps_last_error.argtypes = []
     lib.lmhead_logps_last_error.restype = ctypes.c_char_p
     lib.lmhead_logps_version.argtypes = []
@@ -163,6 +173,32 @@ def raw_bwd_ex(hidden, W, targets, N, H, V, chunk_size, temperature, lse, entrop
                                       int(chunk_size), float(temperature), lse or None, entropy or None,
                                       g_logp or None, g_ent or None, dh or None, dW or None, int(flags),
                                       workspace or None, int(workspace_bytes), stream or None)
+
+
+def raw_fwd_shard(hidden, W_shard, targets, N, H, V_shard, vocab_offset, V_total, chunk_size, temperature,
+                  partial, workspace, workspace_bytes, stream) -> int:
+    """Call lmhead_logps_fwd_shard with integer addresses (0 = NULL); returns the status."""
+    return load().lmhead_logps_fwd_shard(hidden or None, W_shard or None, targets or None, int(N), int(H),
+                                         int(V_shard), int(vocab_offset), int(V_total), int(chunk_size),
+                                         float(temperature), partial or None, workspace or None,
+                                         int(workspace_bytes), stream or None)
+
+
+def raw_merge_shards(partials, P, targets, N, V_total, temperature, logp, entropy, lse, stream) -> int:
+    """Call lmhead_logps_merge_shards with integer addresses (0 = NULL); returns the status."""
+    return load().lmhead_logps_merge_shards(partials or None, int(P), targets or None, int(N), int(V_total),
+                                            float(temperature), logp or None, entropy or None, lse or None,
+                                            stream or None)
+
+
+def raw_bwd_shard(hidden, W_shard, targets, N, H, V_shard, vocab_offset, V_total, chunk_size, temperature, lse,
+                  entropy, g_logp, g_ent, dh, dW_shard, flags, workspace, workspace_bytes, stream) -> int:
+    """Call lmhead_logps_bwd_shard with integer addresses (0 = NULL); returns the status."""
+    return load().lmhead_logps_bwd_shard(hidden or None, W_shard or None, targets or None, int(N), int(H),
+                                         int(V_shard), int(vocab_offset), int(V_total), int(chunk_size),
+                                         float(temperature), lse or None, entropy or None, g_logp or None,
+                                         g_ent or None, dh or None, dW_shard or None, int(flags),
+                                         workspace or None, int(workspace_bytes), stream or None)
 
 
 TRACE_KERNELS = ("fwd_stats_kernel", "fwd_merge_kernel", "bwd_step_kernel", "transpose_kernel",

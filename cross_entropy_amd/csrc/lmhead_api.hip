@@ -178,37 +178,110 @@ int lmhead_logps_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t chunk_
   return ok();
 }
 
-int lmhead_logps_fwd_temp(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
-                          int64_t N, int64_t H, int64_t V, int64_t chunk_size, float temperature,
-                          float* logp, float* entropy, float* lse, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shard ranges: W holds rows [voff, voff + V) of a vocabulary of Vtot ids.
+int check_shard(int64_t V, int64_t voff, int64_t Vtot) {
+  if (voff < 0 || Vtot <= 0 || Vtot >= (int64_t(1) << 31) || voff > Vtot - V)
+    return fail(LMH_ERR_SHAPE, "shard rows [%lld, %lld) must lie in a vocabulary [0, %lld) with 0 < %lld < 2^31",
+                (long long)voff, (long long)(voff + V), (long long)Vtot, (long long)Vtot);
+  return LMH_OK;
+}
+
+// The forward of W's rows [voff, voff + V); writes logp/entropy/lse, or with
+// `rec` the merged partial record of this vocabulary range.
+int fwd_impl(const char* who, const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
+             int64_t N, int64_t H, int64_t V, int64_t voff, int64_t Vtot, int64_t chunk_size,
+             float temperature, float* logp, float* entropy, float* lse, float* rec,
+             void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_shape(N, H, V, chunk_size);
+  if (rc != LMH_OK) return rc;
+  rc = check_shard(V, voff, Vtot);
   if (rc != LMH_OK) return rc;
   rc = check_temperature(temperature);
   if (rc != LMH_OK) return rc;
   if (N == 0) return ok();
-  if (!hidden || !W || !targets || !logp || !lse || !workspace)
-    return fail(LMH_ERR_NULL, "fwd: hidden, W, targets, logp, lse and workspace must be non-NULL");
-  if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(workspace, 16) || !aligned(targets, 4) ||
-      !aligned(logp, 4) || !aligned(lse, 4) || (entropy && !aligned(entropy, 4)))
-    return fail(LMH_ERR_UNSUPPORTED, "fwd: hidden, W and workspace need 16-byte alignment");
+  if (rec == nullptr) {
+    if (!hidden || !W || !targets || !logp || !lse || !workspace)
+      return fail(LMH_ERR_NULL, "%s: hidden, W, targets, logp, lse and workspace must be non-NULL", who);
+    if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(workspace, 16) || !aligned(targets, 4) ||
+        !aligned(logp, 4) || !aligned(lse, 4) || (entropy && !aligned(entropy, 4)))
+      return fail(LMH_ERR_UNSUPPORTED, "%s: hidden, W and workspace need 16-byte alignment", who);
+  } else {
+    if (!hidden || !W || !targets || !workspace)
+      return fail(LMH_ERR_NULL, "%s: hidden, W, targets, partial and workspace must be non-NULL", who);
+    if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(workspace, 16) || !aligned(targets, 4) ||
+        !aligned(rec, 16))
+      return fail(LMH_ERR_UNSUPPORTED, "%s: hidden, W, partial and workspace need 16-byte alignment", who);
+  }
   const lmh::FwdPlan p = lmh::plan_forward(N, H, V);
   if (workspace_bytes < p.bytes)
-    return fail(LMH_ERR_WORKSPACE, "fwd: workspace of %zu bytes, %zu needed", workspace_bytes, p.bytes);
-  lmh::FwdArgs a{hidden, W, targets, N, H, V, p.S, p.n_tt, p.n_vt,
+    return fail(LMH_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes, p.bytes);
+  lmh::FwdArgs a{hidden, W, targets, N, H, V, p.S, p.n_tt, p.n_vt, voff, Vtot,
                  temper_scale(temperature), inv_temperature(temperature), workspace, p.part_ld,
-                 logp, entropy, lse};
+                 logp, entropy, lse, rec};
   const hipError_t e = lmh::launch_fwd(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(LMH_ERR_HIP, "fwd: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(LMH_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();
 }
 
-int lmhead_logps_bwd_ex(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
-                        int64_t N, int64_t H, int64_t V, int64_t chunk_size, float temperature,
-                        const float* lse, const float* entropy, const float* g_logp,
-                        const float* g_ent, float* dh, float* dW, unsigned flags, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+}  // namespace
+
+extern "C" {
+
+int lmhead_logps_fwd_temp(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
+                          int64_t N, int64_t H, int64_t V, int64_t chunk_size, float temperature,
+                          float* logp, float* entropy, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return fwd_impl("fwd", hidden, W, targets, N, H, V, 0, V, chunk_size, temperature, logp, entropy, lse,
+                  nullptr, workspace, workspace_bytes, stream);
+}
+
+int lmhead_logps_fwd_shard(const uint16_t* hidden, const uint16_t* W_shard, const int32_t* targets,
+                           int64_t N, int64_t H, int64_t V_shard, int64_t vocab_offset, int64_t V_total,
+                           int64_t chunk_size, float temperature, float* partial, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (partial == nullptr && N > 0) return fail(LMH_ERR_NULL, "fwd_shard: partial must be non-NULL");
+  return fwd_impl("fwd_shard", hidden, W_shard, targets, N, H, V_shard, vocab_offset, V_total, chunk_size,
+                  temperature, nullptr, nullptr, nullptr, partial, workspace, workspace_bytes, stream);
+}
+
+int lmhead_logps_merge_shards(const float* partials, int64_t P, const int32_t* targets, int64_t N,
+                              int64_t V_total, float temperature, float* logp, float* entropy,
+                              float* lse, void* stream) {
+  if (N < 0 || N >= (int64_t(1) << 31))
+    return fail(LMH_ERR_SHAPE, "merge_shards: N must be in [0, 2^31), got %lld", (long long)N);
+  if (P <= 0 || P > 65536) return fail(LMH_ERR_SHAPE, "merge_shards: P must be in [1, 65536], got %lld", (long long)P);
+  if (V_total <= 0 || V_total >= (int64_t(1) << 31))
+    return fail(LMH_ERR_SHAPE, "merge_shards: V_total must be in (0, 2^31), got %lld", (long long)V_total);
+  int rc = check_temperature(temperature);
+  if (rc != LMH_OK) return rc;
+  if (N == 0) return ok();
+  if (!partials || !targets || !logp || !lse)
+    return fail(LMH_ERR_NULL, "merge_shards: partials, targets, logp and lse must be non-NULL");
+  if (!aligned(partials, 16) || !aligned(targets, 4) || !aligned(logp, 4) || !aligned(lse, 4) ||
+      (entropy && !aligned(entropy, 4)))
+    return fail(LMH_ERR_UNSUPPORTED, "merge_shards: partials need 16-byte alignment");
+  const hipError_t e = lmh::launch_merge(partials, (int)P, N, targets, V_total, inv_temperature(temperature),
+                                         logp, entropy, lse, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LMH_ERR_HIP, "merge_shards: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// The backward of W's rows [voff, voff + V) of a vocabulary of Vtot ids.
+int bwd_impl(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, int64_t N, int64_t H,
+             int64_t V, int64_t voff, int64_t Vtot, int64_t chunk_size, float temperature,
+             const float* lse, const float* entropy, const float* g_logp, const float* g_ent, float* dh,
+             float* dW, unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_shape(N, H, V, chunk_size);
+  if (rc != LMH_OK) return rc;
+  rc = check_shard(V, voff, Vtot);
   if (rc != LMH_OK) return rc;
   rc = check_temperature(temperature);
   if (rc != LMH_OK) return rc;
@@ -240,7 +313,7 @@ int lmhead_logps_bwd_ex(const uint16_t* hidden, const uint16_t* W, const int32_t
   uint16_t* ht = reinterpret_cast<uint16_t*>(ws + p.off_ht);
   hipError_t te = lmh::launch_transpose(W, H, V, H, p.V_pad, p.H_pad, nullptr, V, Wt, p.V_pad, s);
   if (te == hipSuccess)
-    te = lmh::launch_transpose(hidden, H, N, H, p.N_pad, p.H_pad, targets, V, ht, p.N_pad, s);
+    te = lmh::launch_transpose(hidden, H, N, H, p.N_pad, p.H_pad, targets, Vtot, ht, p.N_pad, s);
   if (te != hipSuccess) return fail(LMH_ERR_HIP, "bwd: launch failed: %s", hipGetErrorString(te));
 
   lmh::BwdStep st{};
@@ -250,6 +323,8 @@ int lmhead_logps_bwd_ex(const uint16_t* hidden, const uint16_t* W, const int32_t
   st.N = (int)N;
   st.H = (int)H;
   st.V = (int)V;
+  st.voff = (int)voff;
+  st.Vtot = (int)Vtot;
   st.lse = lse;
   st.entropy = entropy;
   st.g_logp = g_logp;
@@ -301,6 +376,28 @@ int lmhead_logps_bwd_ex(const uint16_t* hidden, const uint16_t* W, const int32_t
     if (e != hipSuccess) return fail(LMH_ERR_HIP, "bwd: launch failed: %s", hipGetErrorString(e));
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int lmhead_logps_bwd_ex(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
+                        int64_t N, int64_t H, int64_t V, int64_t chunk_size, float temperature,
+                        const float* lse, const float* entropy, const float* g_logp,
+                        const float* g_ent, float* dh, float* dW, unsigned flags, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return bwd_impl(hidden, W, targets, N, H, V, 0, V, chunk_size, temperature, lse, entropy, g_logp, g_ent,
+                  dh, dW, flags, workspace, workspace_bytes, stream);
+}
+
+int lmhead_logps_bwd_shard(const uint16_t* hidden, const uint16_t* W_shard, const int32_t* targets,
+                           int64_t N, int64_t H, int64_t V_shard, int64_t vocab_offset, int64_t V_total,
+                           int64_t chunk_size, float temperature, const float* lse, const float* entropy,
+                           const float* g_logp, const float* g_ent, float* dh, float* dW_shard,
+                           unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(hidden, W_shard, targets, N, H, V_shard, vocab_offset, V_total, chunk_size, temperature,
+                  lse, entropy, g_logp, g_ent, dh, dW_shard, flags, workspace, workspace_bytes, stream);
 }
 
 int lmhead_logps_fwd(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, int64_t N,

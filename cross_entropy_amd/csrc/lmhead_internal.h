@@ -41,13 +41,16 @@ struct FwdArgs {
   const int32_t* targets;
   int64_t N, H, V;
   int S, n_tt, n_vt;
-  float sc;     // log2(e) / T
-  float invT;   // 1 / T
+  int64_t voff;   // global id of W's first row (vocabulary shard), 0 for the whole table
+  int64_t Vtot;   // valid target ids are [0, Vtot)
+  float sc;       // log2(e) / T
+  float invT;     // 1 / T
   void* part;
   int64_t part_ld;
   float* logp;
   float* entropy;
   float* lse;
+  float* rec;     // shard partial records [N][4] instead of logp/entropy/lse, or NULL
 };
 
 // One backward launch: the gradient tiles of one block (n_dw + n_dh tiles,
@@ -56,7 +59,8 @@ struct BwdStep {
   const uint16_t* hidden;
   const uint16_t* W;
   const int32_t* targets;
-  int N, H, V;
+  int N, H, V;     // V: rows of W (the shard's vocabulary)
+  int voff, Vtot;  // global id of W's first row; valid target ids are [0, Vtot)
   const float* lse;
   const float* entropy;
   const float* g_logp;
@@ -85,6 +89,9 @@ void trace_begin(hipStream_t stream);
 void trace_end(int kernel, hipStream_t stream, double flops, double bytes);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// merge of P shard records [P][N] (float4 each) into logp / entropy / lse
+hipError_t launch_merge(const float* partials, int P, int64_t N, const int32_t* targets, int64_t Vtot,
+                        float invT, float* logp, float* entropy, float* lse, hipStream_t stream);
 hipError_t launch_bwd_step(const BwdStep& st, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_transpose(const uint16_t* in, int64_t ld_in, int64_t R, int64_t C, int64_t R_pad,

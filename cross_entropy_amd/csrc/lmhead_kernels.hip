@@ -375,11 +375,13 @@ __device__ __forceinline__ Stats merge_stats(Stats a, Stats b) {
 // tiles s, s + S, s + 2S, ... for its 256 tokens (A = W rows = vocabulary,
 // B = hidden rows = tokens) and writes one partial Stats per token and split.
 // sc = log2(e) / T scores the tempered logits z / T in base 2; the target
-// logit is kept untempered (the merge scales it).
+// logit is kept untempered (the merge scales it). W holds the V vocabulary
+// rows from global id voff on (a vocabulary shard; voff = 0 for the whole
+// table): a target is picked here only when it falls inside that range.
 __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W,
-    const int32_t* __restrict__ targets, int N, int H, int V, int S, int n_tt, int n_vt, float sc,
-    float4* __restrict__ part, int64_t part_ld) {
+    const int32_t* __restrict__ targets, int N, int H, int V, int voff, int S, int n_tt, int n_vt,
+    float sc, float4* __restrict__ part, int64_t part_ld) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const int vid = xcd_remap(blockIdx.x, gridDim.x);
   if (vid >= n_tt * S) return;
@@ -396,7 +398,8 @@ __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int tok = tok0 + wn * 64 + j * 32 + (lane & 31);
-    tgt[j] = tok < N ? targets[tok] : -1;
+    const int t = tok < N ? targets[tok] : -1;
+    tgt[j] = (t >= voff && t - voff < V) ? t - voff : -1;   // local row, or no hit
     st[j].m2 = kNegBig;
     st[j].s1 = 0.0f;
     st[j].s2 = 0.0f;
@@ -514,12 +517,14 @@ __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
   }
 }
 
-// Split merge: per token, the S partials in split order, by log-sum-exp.
-// invT = 1 / T tempers the target logit.
+// Split merge: per token, the S partial records in order, by log-sum-exp
+// (vocabulary splits of one launch, or vocabulary shards). invT = 1 / T
+// tempers the target logit; Vtot bounds the valid target ids. With `rec`
+// the merged record itself is written (a shard's partial) instead.
 __global__ __launch_bounds__(256) void fwd_merge_kernel(
     const float4* __restrict__ part, int64_t part_ld, int S, const int32_t* __restrict__ targets,
-    int N, int V, float invT, float* __restrict__ logp, float* __restrict__ entropy,
-    float* __restrict__ lse) {
+    int N, int Vtot, float invT, float* __restrict__ logp, float* __restrict__ entropy,
+    float* __restrict__ lse, float4* __restrict__ rec) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= N) return;
   float4 q = part[i];
@@ -528,8 +533,12 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(
     q = part[(int64_t)s * part_ld + i];
     a = merge_stats(a, Stats{q.x, q.y, q.z, q.w});
   }
+  if (rec != nullptr) {
+    rec[i] = make_float4(a.m2, a.s1, a.s2, a.zt);
+    return;
+  }
   const int t = targets[i];
-  const bool valid = (t >= 0) && (t < V);
+  const bool valid = (t >= 0) && (t < Vtot);
   const float l2s = log2f(a.s1);
   // lse = m + ln(sum e^(z-m)); a +inf logit (and no NaN) leaves m = +inf and
   // s1 = NaN (inf - inf): the log-sum-exp is +inf
@@ -562,7 +571,7 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1;
   const int wn = wave >> 1;
-  const int t0 = s.z_t0, Ct = s.z_Ct, v0 = s.z_v0, Vb = s.z_Vb, H = s.H, V = s.V;
+  const int t0 = s.z_t0, Ct = s.z_Ct, v0 = s.z_v0, Vb = s.z_Vb, H = s.H, Vtot = s.Vtot;
   const int tl0 = tt * kTile;   // token offset in the block
   const int vl0 = vt * kTile;   // vocabulary offset in the block
 
@@ -582,7 +591,7 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
     const int tok = t0 + tl;
     int t = -1;
     if (tl < Ct) t = s.targets[tok];
-    live[j] = (t >= 0) && (t < V);
+    live[j] = (t >= 0) && (t < Vtot);
     const float L = live[j] ? s.lse[tok] : 0.0f;
     const float Hn = (live[j] && s.entropy != nullptr) ? s.entropy[tok] : 0.0f;
     const float ga = (live[j] && s.g_logp != nullptr) ? s.g_logp[tok] : 0.0f;
@@ -592,7 +601,9 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
     c0[j] = -(ga + gb * Hn) * s.invT;
     c1[j] = -(gb * kLn2) * s.invT;
     gl[j] = ga * s.invT;
-    tr[j] = live[j] ? (t - v0 - vw0) : -1;
+    // target row relative to this wave's rows (a target of another shard or
+    // block lands outside [0, 128) or on rows the ragged mask zeroes)
+    tr[j] = live[j] ? (t - s.voff - v0 - vw0) : -1;
   }
   const bool any_dead = __any(!live[0] || !live[1]);
   const bool ragged = (vw0 + 128 > Vb);
@@ -671,7 +682,7 @@ __device__ __forceinline__ void dh_tile(const BwdStep& s, int vid, char* lds) {
   const int wn = wave >> 1;
   const int m0 = mt * kTile;
   const int h0 = hb * kTile;
-  const int H = s.H, V = s.V;
+  const int H = s.H, Vtot = s.Vtot;
   const Operand oa{s.g_dz + (int64_t)m0 * s.ld_dz, s.ld_dz, kTile};
   const Operand ob{s.Wt + (int64_t)h0 * s.ld_wt + s.g_v0, s.ld_wt, kTile};
   f32x16 acc[4][2];
@@ -685,7 +696,7 @@ __device__ __forceinline__ void dh_tile(const BwdStep& s, int vid, char* lds) {
       if (m >= s.g_Ct) continue;
       const int tok = s.g_t0 + m;
       const int t = s.targets[tok];
-      const bool live = (t >= 0) && (t < V);
+      const bool live = (t >= 0) && (t < Vtot);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int n = h0 + wn * 64 + j * 32 + (lane & 31);
@@ -790,7 +801,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   const double N = (double)a.N, H = (double)a.H, V = (double)a.V;
   trace_begin(stream);
   hipLaunchKernelGGL(fwd_stats_kernel, dim3(round8(wg)), dim3(kThreads), 0, stream, a.hidden, a.W,
-                     a.targets, (int)a.N, (int)a.H, (int)a.V, a.S, a.n_tt, a.n_vt, a.sc,
+                     a.targets, (int)a.N, (int)a.H, (int)a.V, (int)a.voff, a.S, a.n_tt, a.n_vt, a.sc,
                      reinterpret_cast<float4*>(a.part), a.part_ld);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -798,10 +809,22 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   trace_begin(stream);
   hipLaunchKernelGGL(fwd_merge_kernel, dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, stream,
                      reinterpret_cast<const float4*>(a.part), a.part_ld, a.S, a.targets, (int)a.N,
-                     (int)a.V, a.invT, a.logp, a.entropy, a.lse);
+                     (int)a.Vtot, a.invT, a.logp, a.entropy, a.lse, reinterpret_cast<float4*>(a.rec));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   trace_end(kFwdMerge, stream, 0.0, 16.0 * a.S * N + 16.0 * N);
+  return hipSuccess;
+}
+
+hipError_t launch_merge(const float* partials, int P, int64_t N, const int32_t* targets, int64_t Vtot,
+                        float invT, float* logp, float* entropy, float* lse, hipStream_t stream) {
+  trace_begin(stream);
+  hipLaunchKernelGGL(fwd_merge_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream,
+                     reinterpret_cast<const float4*>(partials), N, P, targets, (int)N, (int)Vtot, invT,
+                     logp, entropy, lse, nullptr);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  trace_end(kFwdMerge, stream, 0.0, 16.0 * P * (double)N + 16.0 * (double)N);
   return hipSuccess;
 }
 

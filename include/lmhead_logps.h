@@ -193,6 +193,47 @@ int lmhead_logps_bwd_ex(const uint16_t* hidden, const uint16_t* W, const int32_t
                         float* dh, float* dW, unsigned flags,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Vocabulary shards (tunix #2913's head runs sharded, its vocabulary table
+ * split across devices, the per-token (max, exp-sum) partials combined across
+ * shards; the same log-sum-exp combination as blockwise attention's, palingenesis
+ * guide "Long Sequences (SeCO)"). A shard is the rows [vocab_offset,
+ * vocab_offset + V_shard) of a vocabulary of V_total ids; W_shard is bf16
+ * [V_shard, H]; targets are global ids (valid iff 0 <= t < V_total).
+ *
+ * lmhead_logps_fwd_shard: writes, per token, the shard's partial record
+ *   partial f32 [N][4] (16-byte aligned): (m, s1, s2, zt) with m the max of
+ *   the shard's tempered logits in base 2 (log2(e) z / T), s1 = sum 2^(x - m),
+ *   s2 = sum 2^(x - m) (x - m) over x = log2(e) z / T, zt the untempered
+ *   target logit when the target lies in the shard and 0 otherwise. The
+ *   workspace is lmhead_logps_workspace_bytes(N, H, V_shard, chunk_size, 0).
+ * lmhead_logps_merge_shards: merges P records per token in shard order,
+ *   partials f32 [P][N][4], into logp / entropy (or NULL) / lse of the whole
+ *   vocabulary, exactly what lmhead_logps_fwd_temp writes up to float32
+ *   rounding (masked tokens 0). Needs no workspace.
+ * lmhead_logps_bwd_shard: the shard's part of the backward given the merged
+ *   lse / entropy: dW_shard f32 [V_shard, H] and the shard's contribution to
+ *   dh (flags as for lmhead_logps_bwd_ex; on one device, the first shard
+ *   overwrites dh and the others add with LMH_BWD_ACCUMULATE_DH). Workspace:
+ *   lmhead_logps_workspace_bytes(N, H, V_shard, chunk_size, 1).
+ * Errors as for the whole-table calls, plus LMH_ERR_SHAPE when the shard does
+ * not lie in [0, V_total) or P is not in [1, 65536].
+ */
+int lmhead_logps_fwd_shard(const uint16_t* hidden, const uint16_t* W_shard, const int32_t* targets,
+                           int64_t N, int64_t H, int64_t V_shard, int64_t vocab_offset, int64_t V_total,
+                           int64_t chunk_size, float temperature, float* partial,
+                           void* workspace, size_t workspace_bytes, void* stream);
+int lmhead_logps_merge_shards(const float* partials, int64_t P, const int32_t* targets, int64_t N,
+                              int64_t V_total, float temperature,
+                              float* logp, float* entropy, float* lse, void* stream);
+int lmhead_logps_bwd_shard(const uint16_t* hidden, const uint16_t* W_shard, const int32_t* targets,
+                           int64_t N, int64_t H, int64_t V_shard, int64_t vocab_offset, int64_t V_total,
+                           int64_t chunk_size, float temperature,
+                           const float* lse, const float* entropy,
+                           const float* g_logp, const float* g_ent,
+                           float* dh, float* dW_shard, unsigned flags,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Thread-local message of the calling thread's last failing call ("" if none). */
 const char* lmhead_logps_last_error(void);
 

@@ -130,6 +130,31 @@ def test_backward_ex_flags():
     assert "#define LMH_BWD_ACCUMULATE_DH 1u" in src and "#define LMH_BWD_ACCUMULATE_DW 2u" in src
 
 
+def test_shard_errors():
+    """Shard calls reject shards outside [0, V_total) and bad shard counts."""
+    fs = dict(hidden=FAKE, W_shard=FAKE, targets=FAKE, N=64, H=128, V_shard=300, vocab_offset=0, V_total=1000,
+              chunk_size=16, temperature=1.0, partial=FAKE, workspace=FAKE, workspace_bytes=0, stream=0)
+    assert nat.raw_fwd_shard(**dict(fs, vocab_offset=-1)) == -2
+    assert nat.raw_fwd_shard(**dict(fs, vocab_offset=701)) == -2          # 701 + 300 > 1000
+    assert nat.raw_fwd_shard(**dict(fs, V_total=1 << 31)) == -2
+    assert nat.raw_fwd_shard(**dict(fs, partial=0)) == -1
+    assert nat.raw_fwd_shard(**dict(fs, partial=MIS)) == -6
+    assert nat.raw_fwd_shard(**dict(fs, vocab_offset=700)) == -4          # a valid last shard: workspace next
+    ms = dict(partials=FAKE, P=3, targets=FAKE, N=64, V_total=1000, temperature=1.0, logp=FAKE, entropy=FAKE,
+              lse=FAKE, stream=0)
+    assert nat.raw_merge_shards(**dict(ms, P=0)) == -2
+    assert nat.raw_merge_shards(**dict(ms, V_total=0)) == -2
+    assert nat.raw_merge_shards(**dict(ms, partials=0)) == -1
+    assert nat.raw_merge_shards(**dict(ms, temperature=0.0)) == -5
+    assert nat.raw_merge_shards(**dict(ms, N=0)) == 0
+    bs = dict(hidden=FAKE, W_shard=FAKE, targets=FAKE, N=64, H=128, V_shard=300, vocab_offset=0, V_total=1000,
+              chunk_size=16, temperature=1.0, lse=FAKE, entropy=FAKE, g_logp=FAKE, g_ent=FAKE, dh=FAKE,
+              dW_shard=FAKE, flags=0, workspace=FAKE, workspace_bytes=0, stream=0)
+    assert nat.raw_bwd_shard(**dict(bs, vocab_offset=900)) == -2
+    assert nat.raw_bwd_shard(**dict(bs, flags=4)) == -5
+    assert nat.raw_bwd_shard(**bs) == -4
+
+
 def test_workspace_query_errors():
     import ctypes
     assert nat.load().lmhead_logps_workspace_bytes(1, 64, 10, 4, 0, None) == -1
