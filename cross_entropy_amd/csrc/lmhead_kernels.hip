@@ -575,6 +575,23 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
   const int tl0 = tt * kTile;   // token offset in the block
   const int vl0 = vt * kTile;   // vocabulary offset in the block
 
+  // per-token inputs, loaded before the K loop so their latency hides behind
+  // it; indices are clamped so every load is unconditional (a conditional load
+  // per value costs a full memory round trip each)
+  int t_in[2];
+  float l_in[2], e_in[2], gl_in[2], ge_in[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int tl = tl0 + wn * 64 + j * 32 + (lane & 31);
+    const int tok = t0 + min(tl, Ct - 1);
+    t_in[j] = s.targets[tok];
+    if (tl >= Ct) t_in[j] = -1;
+    l_in[j] = s.lse[tok];
+    e_in[j] = s.entropy != nullptr ? s.entropy[tok] : 0.0f;
+    gl_in[j] = s.g_logp != nullptr ? s.g_logp[tok] : 0.0f;
+    ge_in[j] = s.g_ent != nullptr ? s.g_ent[tok] : 0.0f;
+  }
+
   const Operand oa{s.W + (int64_t)(v0 + vl0) * H, H, min(kTile, Vb - vl0)};
   const Operand ob{s.hidden + (int64_t)(t0 + tl0) * H, H, min(kTile, Ct - tl0)};
   f32x16 acc[4][2];
@@ -587,15 +604,14 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
   const int vw0 = vl0 + wm * 128;   // block-local vocabulary row of this wave
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int tl = tl0 + wn * 64 + j * 32 + (lane & 31);
-    const int tok = t0 + tl;
-    int t = -1;
-    if (tl < Ct) t = s.targets[tok];
+    const int t = t_in[j];
     live[j] = (t >= 0) && (t < Vtot);
-    const float L = live[j] ? s.lse[tok] : 0.0f;
-    const float Hn = (live[j] && s.entropy != nullptr) ? s.entropy[tok] : 0.0f;
-    const float ga = (live[j] && s.g_logp != nullptr) ? s.g_logp[tok] : 0.0f;
-    const float gb = (live[j] && s.g_ent != nullptr) ? s.g_ent[tok] : 0.0f;
+    // masked tokens: every input is replaced (selected, never multiplied), so
+    // whatever their rows hold cannot reach dz
+    const float L = live[j] ? l_in[j] : 0.0f;
+    const float Hn = live[j] ? e_in[j] : 0.0f;
+    const float ga = live[j] ? gl_in[j] : 0.0f;
+    const float gb = live[j] ? ge_in[j] : 0.0f;
     nlseL[j] = -L * kLog2e;
     // dz = p * (c1 * d + c0) (+ g_l / T at the target), d = log2 p
     c0[j] = -(ga + gb * Hn) * s.invT;
@@ -637,12 +653,72 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
   }
 }
 
+// Writes a wave's 128 x 64 accumulator block into a float32 matrix (row
+// r_base + acc_row(i, r, lane), column c_base + 32 j + lane % 32; rows at or
+// past `rows` and columns at or past `cols` are skipped), storing or adding.
+// Rows whose target is masked (`targets` given, id outside [0, Vtot)) are
+// stored as 0, or left unchanged when adding. The read-modify-write is
+// batched per 32-row sub-block: its loads (and target ids) are all in flight
+// before the first add; one load-add-store per element would wait out the
+// whole memory latency 128 times per lane.
+__device__ __forceinline__ void write_acc(float* __restrict__ out, int64_t ld, int r_base, int rows,
+                                          int c_base, int cols, bool add, const int32_t* __restrict__ targets,
+                                          int t_base, int Vtot, const f32x16 (&acc)[4][2]) {
+  const int lane = threadIdx.x & 63;
+  bool col_ok[2];
+  int col[2];   // clamped into range, so every load below is unconditional
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = c_base + j * 32 + (lane & 31);
+    col_ok[j] = c < cols;
+    col[j] = col_ok[j] ? c : cols - 1;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float old[16][2];
+    bool row_ok[16], live[16];
+    int row[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = r_base + acc_row(i, r, lane);
+      row_ok[r] = m < rows;
+      row[r] = row_ok[r] ? m : rows - 1;
+      live[r] = true;
+    }
+    if (targets != nullptr) {
+      int t[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t[r] = targets[t_base + row[r]];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) live[r] = (t[r] >= 0) && (t[r] < Vtot);
+    }
+    if (add) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) old[r][j] = out[(int64_t)row[r] * ld + col[j]];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (!(row_ok[r] && col_ok[j])) continue;
+        float* p = out + (int64_t)row[r] * ld + col[j];
+        if (add) {
+          if (live[r]) *p = old[r][j] + acc[i][j][r];
+        } else {
+          *p = live[r] ? acc[i][j][r] : 0.0f;
+        }
+      }
+    }
+  }
+}
+
 // dW tile: dW[v0 + m][n] (+)= sum_k dz[k][m] ht[n][t0 + k] over the block's
 // tokens (A = dz read MN-contiguous, B = hidden^T with masked tokens zeroed).
 __device__ __forceinline__ void dw_tile(const BwdStep& s, int vid, char* lds) {
   int mt, hb;
   raster(vid, s.n_dw / s.n_ht, s.n_ht, 4, mt, hb);
-  const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1;
   const int wn = wave >> 1;
@@ -654,59 +730,28 @@ __device__ __forceinline__ void dw_tile(const BwdStep& s, int vid, char* lds) {
   f32x16 acc[4][2];
   Pipe pipe;
   mma_tile<true>(oa, ob, (s.g_Ct + kBK - 1) / kBK * kBK, lds, acc, pipe);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * 128 + acc_row(i, r, lane);
-      if (m >= s.g_Vb) continue;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = h0 + wn * 64 + j * 32 + (lane & 31);
-        if (n < H) {
-          float* p = s.dW + (int64_t)(s.g_v0 + m) * H + n;
-          *p = s.g_acc_dW ? (*p + acc[i][j][r]) : acc[i][j][r];
-        }
-      }
-    }
+  write_acc(s.dW + (int64_t)s.g_v0 * H, H, m0 + wm * 128, s.g_Vb, h0 + wn * 64, H, s.g_acc_dW != 0,
+            nullptr, 0, 0, acc);
 }
 
 // dh tile: dh[t0 + m][n] (+)= sum_k dz[m][k] Wt[n][v0 + k] over the block's
-// vocabulary; masked token rows are written as 0.
+// vocabulary; masked token rows are written as 0 (left alone when adding).
 __device__ __forceinline__ void dh_tile(const BwdStep& s, int vid, char* lds) {
   int mt, hb;
   raster(vid, s.n_dh / s.n_ht, s.n_ht, 4, mt, hb);
-  const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1;
   const int wn = wave >> 1;
   const int m0 = mt * kTile;
   const int h0 = hb * kTile;
-  const int H = s.H, Vtot = s.Vtot;
+  const int H = s.H;
   const Operand oa{s.g_dz + (int64_t)m0 * s.ld_dz, s.ld_dz, kTile};
   const Operand ob{s.Wt + (int64_t)h0 * s.ld_wt + s.g_v0, s.ld_wt, kTile};
   f32x16 acc[4][2];
   Pipe pipe;
   mma_tile<false>(oa, ob, (s.g_Vb + kBK - 1) / kBK * kBK, lds, acc, pipe);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * 128 + acc_row(i, r, lane);
-      if (m >= s.g_Ct) continue;
-      const int tok = s.g_t0 + m;
-      const int t = s.targets[tok];
-      const bool live = (t >= 0) && (t < Vtot);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = h0 + wn * 64 + j * 32 + (lane & 31);
-        if (n < H) {
-          float* p = s.dh + (int64_t)tok * H + n;
-          const float v = live ? acc[i][j][r] : 0.0f;
-          *p = s.g_acc_dh ? (*p + v) : v;
-        }
-      }
-    }
+  write_acc(s.dh + (int64_t)s.g_t0 * H, H, m0 + wm * 128, s.g_Ct, h0 + wn * 64, H, s.g_acc_dh != 0,
+            s.targets, s.g_t0, s.Vtot, acc);
 }
 
 // One backward launch: each XCD (workgroups are dealt to the 8 XCDs
