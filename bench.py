@@ -61,7 +61,7 @@ def stored_traffic(kernel: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(h_bits, W_bits, targets, chunk, g_l, g_e, sample: int):
+def cpu_baseline(h_bits, W_bits, targets, chunk, g_l, g_e, sample: int, N: int):
     """The fp64 oracle, as it stands, on `sample` tokens of the same inputs
     (forward + backward of those tokens; dW over them)."""
     import numpy as np
@@ -83,7 +83,7 @@ def cpu_baseline(h_bits, W_bits, targets, chunk, g_l, g_e, sample: int):
         "unit": "tokens/s",
         "cores": int(max(threads) if threads else 1),
         "kind": "oracle",
-        "sample": f"{idx.size} sampled tokens of the N=65536 workload, fp64 forward+backward "
+        "sample": f"{idx.size} sampled tokens of the N={N} workload, fp64 forward+backward "
                   f"(full logits row per token, dW over the sample), {dt:.1f} s",
     }
 
@@ -95,6 +95,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--cpu-sample", type=int, default=64, help="tokens the CPU oracle runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", type=int, default=WORKLOAD_INDEX, choices=(1, 2, 3, 4, 5),
+                    help="synthetic workload (default 3, the batch-16 x 4096 headline; the others are "
+                         "the one-sequence head, the context-rank share and the pad-first packed row)")
+    ap.add_argument("--chunk", type=int, default=0, help="chunk_size override (workload 4 runs 1024 and 4096)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times), the known-size "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -121,8 +125,8 @@ def main() -> int:
     from cross_entropy_amd import _native
     from synthetic import CONFIGS, make_cotangents, make_inputs
 
-    cfg = CONFIGS[WORKLOAD_INDEX]
-    N, H, V, C = cfg.N, cfg.H, cfg.V, cfg.chunk_size
+    cfg = CONFIGS[args.workload]
+    N, H, V, C = cfg.N, cfg.H, cfg.V, (args.chunk or cfg.chunk_size)
     lm.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -209,8 +213,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "N": N, "H": H, "V": V, "chunk_size": C, "batch": 16,
-                   "seq_len": 4096, "parallelism": "none (one GPU)"},
+        "config": dict({"workload": cfg.name, "N": N, "H": H, "V": V, "chunk_size": C},
+                       **({"batch": 16, "seq_len": 4096} if args.workload == 3 else {}),
+                       parallelism="none (one GPU)"),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "tflops_credited": round(tflops, 1),
         "tflops_executed": round(executed / (ms_step * 1e-3) / 1e12, 1),
@@ -224,7 +229,10 @@ def main() -> int:
         out["cpu_baseline"] = None
     else:
         log(f"[bench] CPU oracle on {args.cpu_sample} sampled tokens")
-        out["cpu_baseline"] = cpu_baseline(h_bits, W_bits, targets, C, g_l, g_e, args.cpu_sample)
+        out["cpu_baseline"] = cpu_baseline(h_bits, W_bits, targets, C, g_l, g_e, args.cpu_sample, N)
+    real = int(np.count_nonzero((targets >= 0) & (targets < V)))
+    if real != N:   # padded workloads: the rate of real (unmasked) tokens as well
+        out["real_tokens_per_s"] = round(real * args.steps / elapsed, 1)
     print(json.dumps(out), flush=True)
     return 0
 

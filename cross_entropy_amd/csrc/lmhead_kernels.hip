@@ -755,25 +755,32 @@ __device__ __forceinline__ void dh_tile(const BwdStep& s, int vid, char* lds) {
 }
 
 // One backward launch: each XCD (workgroups are dealt to the 8 XCDs
-// round-robin) takes an equal share of the gradient tiles, then an equal
-// share of the cotangent tiles, so the long tiles start first everywhere and
-// the short ones fill the tail.
+// round-robin) takes an equal share of each kind of tile: its eighth of the
+// dW tiles and of the dh tiles (the kind with the longer K first), then its
+// eighth of the cotangent tiles, so the long tiles start first everywhere and
+// the short ones fill the tail. (Cutting the concatenated gradient-tile list
+// into eight ranges instead piles all dh tiles onto the last XCDs, which
+// doubles their share of the work when the two kinds' K differ.)
 __global__ __launch_bounds__(kThreads) void bwd_step_kernel(const BwdStep s) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const int xcd = blockIdx.x & 7;
   const int loc = blockIdx.x >> 3;
-  const int n_g = s.n_dw + s.n_dh;
   const int n_z = s.z_ntt * s.z_nvt;
-  const int g_lo = xcd * n_g / 8;
-  const int g_cnt = (xcd + 1) * n_g / 8 - g_lo;
+  const int dw_lo = xcd * s.n_dw / 8;
+  const int dw_cnt = (xcd + 1) * s.n_dw / 8 - dw_lo;
+  const int dh_lo = xcd * s.n_dh / 8;
+  const int dh_cnt = (xcd + 1) * s.n_dh / 8 - dh_lo;
   const int z_lo = xcd * n_z / 8;
   const int z_cnt = (xcd + 1) * n_z / 8 - z_lo;
+  const bool dh_first = s.g_Vb > s.g_Ct;   // dh tiles run K = Vb, dW tiles K = Ct
+  const int first_cnt = dh_first ? dh_cnt : dw_cnt;
+  const int g_cnt = dw_cnt + dh_cnt;
   if (loc < g_cnt) {
-    const int g = g_lo + loc;
-    if (g < s.n_dw) {
-      dw_tile(s, g, lds);
+    const bool is_dh = (loc < first_cnt) == dh_first;
+    if (is_dh) {
+      dh_tile(s, dh_lo + (dh_first ? loc : loc - dw_cnt), lds);
     } else {
-      dh_tile(s, g - s.n_dw, lds);
+      dw_tile(s, dw_lo + (dh_first ? loc - dh_cnt : loc), lds);
     }
   } else if (loc - g_cnt < z_cnt) {
     dz_tile(s, z_lo + loc - g_cnt, lds);
@@ -878,7 +885,8 @@ hipError_t launch_bwd_step(const BwdStep& st, hipStream_t stream) {
   const int n_z = st.z_ntt * st.z_nvt;
   int per = 0;
   for (int x = 0; x < 8; ++x)
-    per = max(per, ((x + 1) * n_g / 8 - x * n_g / 8) + ((x + 1) * n_z / 8 - x * n_z / 8));
+    per = max(per, ((x + 1) * st.n_dw / 8 - x * st.n_dw / 8) + ((x + 1) * st.n_dh / 8 - x * st.n_dh / 8) +
+                       ((x + 1) * n_z / 8 - x * n_z / 8));
   if (per == 0) return hipSuccess;
   const double H = (double)st.H;
   const double gc = (double)st.g_Ct, gv = (double)st.g_Vb;
