@@ -142,6 +142,17 @@ int check_shape(int64_t N, int64_t H, int64_t V, int64_t chunk_size) {
   return LMH_OK;
 }
 
+// The backward's GEMMs read 256-row tiles of the transposed W and hidden
+// states (row strides V_pad and N_pad elements) through 32-bit byte offsets
+// from the tile's base: 256 * stride * 2 bytes must stay below 2^32.
+int check_backward_size(int64_t N, int64_t V) {
+  const int64_t lim = int64_t(1) << 23;
+  if (lmh::round_up(std::max<int64_t>(N, 1), lmh::kTileRows) >= lim || lmh::round_up(V, lmh::kTileRows) >= lim)
+    return fail(LMH_ERR_UNSUPPORTED, "bwd: N (%lld) and V (%lld) rounded up to 256 must stay below 2^23",
+                (long long)N, (long long)V);
+  return LMH_OK;
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // Base-2 scale of the tempered logits and the reciprocal temperature; at
@@ -172,6 +183,10 @@ int lmhead_logps_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t chunk_
   if (bytes_out == nullptr) return fail(LMH_ERR_NULL, "bytes_out is NULL");
   const int rc = check_shape(N, H, V, chunk_size);
   if (rc != LMH_OK) return rc;
+  if (with_backward) {
+    const int rb = check_backward_size(N, V);
+    if (rb != LMH_OK) return rb;
+  }
   size_t b = lmh::plan_forward(N, H, V).bytes;
   if (with_backward) b = std::max(b, lmh::plan_backward(N, H, V, chunk_size).bytes);
   *bytes_out = b;
@@ -292,6 +307,8 @@ int bwd_impl(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, 
   if (g_ent != nullptr && entropy == nullptr)
     return fail(LMH_ERR_ARGS, "bwd: g_ent given without the forward's entropy");
   if (!dW) return fail(LMH_ERR_NULL, "bwd: dW must be non-NULL");
+  rc = check_backward_size(N, V);
+  if (rc != LMH_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (N == 0) {
     if (acc_dW) return ok();   // nothing to add

@@ -12,22 +12,27 @@
 //             gradient matmuls (dh = dz W, dW = dz^T h) read that one dz.
 //
 // Every contraction runs on one MFMA tile core: a 256 x 256 output tile per
-// 512-thread workgroup (8 wave64s as 2 x 4, each owning 128 x 64),
-// v_mfma_f32_32x32x16_bf16, with both operands K-contiguous. K is staged
-// through two 64-wide LDS slices filled by direct-to-LDS loads
-// (global_load_lds_dwordx4): the next slice lands while the current one is
-// consumed and no VGPRs hold staged data. Slice rows are 128 bytes with a
-// 16-byte-chunk XOR swizzle, which keeps the MFMA fragment reads free of
-// bank conflicts. The MFMA block of each slice runs at raised wave priority
-// so the two waves sharing a SIMD keep its matrix pipe fed. Operands that are stored MN-contiguous (W and hidden in
-// the backward) are given to the core through transposed copies.
+// 256-thread workgroup (4 wave64s as 2 x 2, each owning 128 x 128, its 256
+// f32 accumulators in AGPRs), v_mfma_f32_16x16x32_bf16. One wave per SIMD
+// halves the LDS fragment traffic per MFMA against two waves of 128 x 64,
+// and the short 16x16 MFMA keeps accumulator traffic through the register
+// file low; the wave hides its own latencies through the order in which it
+// issues work (see mma_tile). K is staged through two 64-wide LDS slices
+// filled by direct-to-LDS loads (global_load_lds_dwordx4), so no VGPRs hold
+// staged data. Slice rows are 128 bytes with a 16-byte-chunk XOR swizzle,
+// which keeps the fragment reads free of bank conflicts. Operands stored
+// MN-contiguous are read with transposed LDS reads (the dW GEMM's cotangent)
+// or given to the core through transposed copies (W and hidden in the
+// backward).
 //
-// MFMA 32x32x16 register layout used throughout (wave64): lane l supplies
-// row (l % 32) of A and column (l % 32) of B with the 8 K values
-// 8*(l/32) .. 8*(l/32)+7; result register r of lane l holds
-// D[8*(r/4) + 4*(l/32) + (r%4)][l % 32].
+// MFMA 16x16x32 register layout used throughout (wave64): lane l supplies
+// row (l % 16) of A and column (l % 16) of B with the 8 K values
+// 8*(l/16) .. 8*(l/16)+7; result register r of lane l holds
+// D[4*(l/16) + r][l % 16].
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "lmhead_internal.h"
 
@@ -35,21 +40,20 @@ namespace lmh {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;                    // 4 waves
 constexpr int kTile = 256;                       // output tile edge
 constexpr int kBK = 64;                          // K per LDS slice
-constexpr int kStages = 2;                       // slices in the ring
 constexpr int kRowBytes = kBK * 2;               // 128 B per staged row
-constexpr int kRowsPerDma = 1024 / kRowBytes;    // rows one wave-wide DMA fills
-constexpr int kOpBytes = kTile * kRowBytes;      // 16 KB per operand slice
+constexpr int kOpBytes = kTile * kRowBytes;      // 32 KB per operand slice
 constexpr int kStageBytes = 2 * kOpBytes;        // A + B
-constexpr int kLdsBytes = kStages * kStageBytes; // 128 KB of the 160 KB per CU
-
-constexpr int kTPitch = kTile * 2 + 16;          // staged transposed cotangent row (bytes)
-constexpr int kDzLdsBytes = kTile * kTPitch > kLdsBytes ? kTile * kTPitch : kLdsBytes;
+constexpr int kRingBytes = 2 * kStageBytes;      // two slices in flight
+constexpr int kLdsBytes = kRingBytes + 1024;     // + a 1 KB scratch row (see mma_tile)
+constexpr int kNB = 8;                           // 16-wide MFMA blocks per wave edge
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
@@ -65,10 +69,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v = {lo, hi};
   bf16x2 b = __builtin_convertvector(v, bf16x2);   // round to nearest even
   return __builtin_bit_cast(uint32_t, b);
-}
-
-__device__ __forceinline__ uint16_t to_bf16(float x) {
-  return (uint16_t)(pack_bf16x2(x, 0.0f) & 0xFFFFu);
 }
 
 // Workgroup id -> virtual id such that each XCD (workgroups are dealt to the
@@ -91,10 +91,22 @@ __device__ __forceinline__ void raster(int vid, int n_m, int n_n, int group, int
   tn = in / gsz;
 }
 
+// Wave index as a scalar, so the per-wave LDS and address arithmetic stays
+// on the scalar unit.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Pin a 4-register accumulator block in AGPRs up to this point: the
+// epilogue's reads of it then become copies right here, instead of one bulk
+// copy of all 256 accumulators into VGPRs at the end of the loop.
+__device__ __forceinline__ void pin_acc(f32x4& a) { asm volatile("" : "+a"(a)); }
+
 // ---------------------------------------------------------------------------
-// Staging. A K-contiguous operand: element (row, k) at base[row * ld + k];
-// rows at or past `rows` read row rows-1 instead (their results are
-// discarded or masked by the epilogues), so every load stays in bounds.
+// Staging. An operand of the core: a K-contiguous operand holds element
+// (row, k) at base[row * ld + k], rows at or past `rows` are read as row
+// rows-1 (their results are discarded or masked by the epilogues), so every
+// load stays in bounds; an MN-contiguous operand holds element (m, k) at
+// base[k * ld + m]. Byte offsets within a tile stay below 2^32 (the host
+// bounds ld).
 struct Operand {
   const uint16_t* base;
   int64_t ld;
@@ -102,20 +114,24 @@ struct Operand {
 };
 
 // XOR applied to the 16-byte chunk index of staged row r (8 chunks per row):
-// any 16 consecutive rows read at one logical chunk hit 16 distinct 16-byte
-// bank groups of the 256-byte bank line.
+// 8 consecutive rows read at one logical chunk hit 8 distinct 16-byte bank
+// groups of the 128-byte bank line.
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
+
+// MN-contiguous slice rows (64 K-rows of 256 m, 512 bytes each): chunk XOR by
+// 2 * (k % 4), so the 4 K-rows one 16-lane group of a transposed read visits
+// land on distinct bank groups.
+__device__ __forceinline__ int swz_mn(int k) { return 2 * (k & 3); }
 
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
 // One direct-to-LDS load: 64 lanes x 16 B land at m0 + 16 * lane; lane l
-// reads 16 bytes at sbase + voff(l) (scalar base, 32-bit per-lane offset,
-// so a wave's loads cost one VGPR each). Issued as inline asm so the
-// compiler does not add a vmcnt(0) in front of every LDS read of the ring;
-// completion is awaited explicitly (wait_vm) before the barrier that
-// publishes a slice.
+// reads 16 bytes at sbase + voff(l) (scalar base, 32-bit per-lane offset).
+// Issued as inline asm so the compiler does not add a vmcnt(0) in front of
+// every LDS read of the ring; completion is awaited explicitly (wait_vm)
+// before the barrier that publishes a slice.
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds_wave_base) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
                "s"(lds_wave_base)
@@ -128,226 +144,289 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Stage rows [0, 256) x K [k0, k0 + 64) of one operand. Each wave loads 32
-// rows as 4 x 8 rows of 8 chunks; lane l fills physical chunk l % 8 of row
-// l / 8 with the logical chunk that the swizzle puts there. Byte offsets
-// from op.base stay below 2^32: a tile spans 256 rows.
-__device__ __forceinline__ void stage(const Operand& op, int k0, uint32_t lds_op) {
+// Per-lane byte offsets of a wave's 8 loads of one operand slice. Load q of
+// wave w fills 1 KB of the slice at byte 8 KB * w + 1 KB * q:
+//  K-contiguous: rows 64 w + 8 q .. +7; lane l fills physical chunk l % 8
+//    of row 64 w + 8 q + l / 8 with the logical chunk the swizzle puts there;
+//  MN-contiguous: K-rows 16 w + 2 q, +1; lane l fills physical chunk l % 32
+//    of K-row 16 w + 2 q + l / 32 likewise.
+struct LoadOffs {
+  uint32_t o[8];
+};
+
+template <bool MN>
+__device__ __forceinline__ LoadOffs load_offsets(const Operand& op) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const char* b = reinterpret_cast<const char*>(op.base) + 2 * (int64_t)k0;
+  LoadOffs d;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r0 = wave * 32 + q * kRowsPerDma;
-    const int r = r0 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    const int rr = min(r, op.rows - 1);
-    const uint32_t off = (uint32_t)((int64_t)rr * op.ld * 2) + (uint32_t)(c * 16);
-    dma16(off, b, __builtin_amdgcn_readfirstlane(lds_op + r0 * kRowBytes));
+  for (int q = 0; q < 8; ++q) {
+    if (MN) {
+      const int r = wave * 16 + 2 * q + (lane >> 5);
+      const int c = (lane & 31) ^ swz_mn(r);
+      d.o[q] = (uint32_t)((int64_t)r * op.ld * 2) + (uint32_t)(c * 16);
+    } else {
+      const int r = wave * 64 + 8 * q + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      const int rr = min(r, op.rows - 1);
+      d.o[q] = (uint32_t)((int64_t)rr * op.ld * 2) + (uint32_t)(c * 16);
+    }
   }
+  return d;
 }
 
-// Stage K-rows [k0, k0 + 64) x M [0, 256) of an MN-contiguous operand:
-// element (m, k) at base[k * ld + m]. The slice holds 64 rows of 256 m
-// (512 B each); 16-byte chunks are XOR-swizzled by 4 * (k % 4) so the
-// transposed fragment reads below hit distinct bank groups. Each wave-wide
-// DMA fills two rows.
-__device__ __forceinline__ void stage_mn(const Operand& op, int k0, uint32_t lds_op) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const char* b = reinterpret_cast<const char*>(op.base + (int64_t)k0 * op.ld);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r0 = wave * 8 + q * 2;
-    const int r = r0 + (lane >> 5);
-    const int c = (lane & 31) ^ (4 * (r & 3));
-    const uint32_t off = (uint32_t)((int64_t)r * op.ld * 2) + (uint32_t)(c * 16);
-    dma16(off, b, __builtin_amdgcn_readfirstlane(lds_op + r0 * (kTile * 2)));
-  }
+// Scalar base of a slice load: an operand starting at `base` (row stride
+// ld) at K offset k0, in SGPRs.
+template <bool MN>
+__device__ __forceinline__ const void* slice_base(const uint16_t* base, int64_t ld, int k0) {
+  const char* b = reinterpret_cast<const char*>(base) + 2 * (MN ? (int64_t)k0 * ld : (int64_t)k0);
+  const uint64_t bu = reinterpret_cast<uint64_t>(b);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bu);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bu >> 32));
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
 }
-
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) short4v* lds_s4;
 
 // LDS transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane j
 // receives element (j & 3) of the 8-byte reads of lanes (j >> 2) + 4q,
-// q = 0..3. Pointing lane s of the group at row k + (s >> 2), columns
+// q = 0..3. Pointing lane s of the group at K-row k + (s >> 2), columns
 // m + 4 (s & 3) .. +3 therefore hands lane j the 4 consecutive K values
 // (k .. k+3) of column m + j.
 __device__ __forceinline__ short4v ds_read_tr(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s4)(const __attribute__((address_space(3))) char*)p);
+  typedef __attribute__((address_space(3))) short4v* lds_s4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(const __attribute__((address_space(3))) char*)p);
 }
 
-// Scheduling pins. NM MFMAs of one 16-deep step with the NR LDS reads of the
-// next step spread between them, front-loaded: after MFMA q come
-// ceil((q+1) NR / NM) - ceil(q NR / NM) reads. The compiler's own order
-// issues the reads late and waits on them at once, which exposes the LDS
-// latency to the matrix pipe several times per slice.
-template <int NM, int NR, int Q>
-struct Pin {
-  static __device__ __forceinline__ void run() {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-    constexpr int n = ((Q + 1) * NR + NM - 1) / NM - (Q * NR + NM - 1) / NM;
-    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);   // n LDS reads
-    Pin<NM, NR, Q + 1>::run();
-  }
-};
-template <int NM, int NR>
-struct Pin<NM, NR, NM> {
-  static __device__ __forceinline__ void run() {}
-};
-
-// The tile core: acc[i][j] (wave sub-block i of 32 A-rows, j of 32 B-rows)
-// = sum over k < K of A[row][k] * B[row][k]. K is a multiple of 64. With
-// A_MN the A operand is MN-contiguous (see stage_mn) and its fragments are
-// assembled with transposed LDS reads. Ends with a barrier, so LDS may be
-// reused as soon as it returns.
+// ---------------------------------------------------------------------------
+// The tile core: acc[i][j] (wave block i of 16 A-rows, j of 16 B-rows)
+// = sum over k < K of A[row][k] * B[row][k]; K a multiple of 64. With A_MN the
+// A operand is MN-contiguous and its fragments are assembled with two
+// transposed reads each.
 //
-// Schedule of one 64-deep slice k (4 steps of 16): the fragments of step
-// s + 1 are read into the other register set between the 8 MFMAs of step s
-// (pinned, in the order the MFMAs consume them); the loads of slice k + 1
-// are issued at the start of steps 0 (A) and 1 (B); the barrier that
-// publishes slice k + 1 sits halfway through the MFMAs of the last step, and
-// the first fragments of slice k + 1 are read right after it, between the
-// remaining MFMAs, so the matrix pipe never restarts from an empty register
-// set. The last slice is peeled off so the steady-state body has no branch.
+// A slice is 2 steps of 32 K; a step is 64 MFMAs (8 x 8 blocks, i-major:
+// A fragment i serves MFMAs 8 i .. 8 i + 7, B fragment j every eighth).
+// Schedule, in 16-cycle MFMA slots:
+//  * B fragments are double buffered: those of step s + 1 are read one every
+//    other MFMA at the start of step s. A fragments are single buffered:
+//    fragment i of step s + 1 is read right after its last MFMA of step s,
+//    57 MFMAs ahead of its first use (this frees 32 VGPRs);
+//  * the loads of slice k + 2 go into the LDS slot slice k frees, one every
+//    4 MFMAs over the first 64 slots after the barrier that frees it: a burst
+//    of loads stalls the wave's issue, and with one wave per SIMD nothing
+//    else feeds the matrix pipe meanwhile;
+//  * that barrier, which also publishes slice k + 1, sits halfway through the
+//    last step of slice k; the reads of slice k + 1's first step follow it.
+// The loop body runs from that barrier to the next, so its back edge falls
+// where every pending LDS read was issued long before. Every iteration runs
+// the same code: where no slice k + 2 exists its loads go to the scratch row
+// (and are awaited like the others by the next iteration), so there is no
+// branch (and no merge of 256 accumulator registers) in the loop. The last
+// iteration, outside the loop, issues loads only for a chained next tile.
 //
 // Chaining tiles (the forward's walk over vocabulary tiles): `pipe` holds the
-// LDS slot of the tile's first slice and whether that slice was already
-// issued; with `next` the last slice issues the first slice of the next tile
-// (same operand shapes) into the free slot, so the next tile starts on data
-// that landed during this tile's epilogue.
+// LDS slot of the tile's first slice and how many of its slices the previous
+// tile already issued; with `chain` the loads run on into the next tile, whose
+// operands have the same shapes as this tile's (ld, rows, K) and start at
+// nA_base and nB_base, so it starts on data that landed during this tile's
+// epilogue. Ends with a barrier unless chained, so LDS may be reused.
 struct Pipe {
-  int slot = 0;         // LDS slot (0 or 1) of the first slice
-  bool staged = false;  // its loads were issued by the previous tile
+  int slot = 0;     // LDS slot (0 or 1) of the first slice
+  int staged = 0;   // slices of this tile already issued (slice 0 then also published)
 };
 
 template <bool A_MN>
 __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int K, char* lds,
-                                         f32x16 (&acc)[4][2], Pipe& pipe,
-                                         const Operand* nextA = nullptr, const Operand* nextB = nullptr) {
+                                         f32x4 (&acc)[kNB][kNB], Pipe& pipe, const uint16_t* nA_base,
+                                         const uint16_t* nB_base, bool chain) {
+  constexpr int NM = kNB * kNB;            // MFMAs per step
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1;
   const int wn = wave >> 1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
   const uint32_t base = lds_offset(lds);
+  const uint32_t scratch_row = base + kRingBytes;
   const int nk = K / kBK;
-  const int sw = swz(lane & 31);
-  const int a_off = (wm * 128 + (lane & 31)) * kRowBytes;
-  const int b_off = kOpBytes + (wn * 64 + (lane & 31)) * kRowBytes;
-  // transposed A reads: lane group gq = lane / 16 covers columns
-  // 16 * (gq & 1) .. +15 of a 32-column sub-block and K rows 8 * (gq >> 1) ..
-  const int gq = lane >> 4;
-  const int sl = lane & 15;
-  const int t_row = 8 * (gq >> 1) + (sl >> 2);             // + 16 ks (+ 4 for the upper half)
-  const int t_chunk = wm * 16 + 2 * (gq & 1) + ((sl & 3) >> 1);   // + 4 i, before the swizzle
-  const int t_byte = 8 * (sl & 1);
-
-  bf16x8 fa[2][4], fb[2][2];
-  auto read_a = [&](const char* cur, int ks, int co, int buf, int i) {
-    if (A_MN) {
-      const int row = ks * 16 + t_row;          // row & 3 == (row + 4) & 3
-      const int x = row & 3;
-      const char* p = cur + row * (kTile * 2) + ((t_chunk | ((i ^ x) << 2)) << 4) + t_byte;
-      const short4v lo = ds_read_tr(p);
-      const short4v hi = ds_read_tr(p + 4 * (kTile * 2));
-      const short4v v8[2] = {lo, hi};
-      fa[buf][i] = __builtin_bit_cast(bf16x8, v8);
-    } else {
-      fa[buf][i] = *reinterpret_cast<const bf16x8*>(cur + a_off + i * 32 * kRowBytes + co);
-    }
-  };
-  auto read_b = [&](const char* cur, int co, int buf, int j) {
-    fb[buf][j] = *reinterpret_cast<const bf16x8*>(cur + b_off + j * 32 * kRowBytes + co);
-  };
-  // in the order the MFMAs (i-major) consume them
   const int p0 = pipe.slot;
-  auto read_frags = [&](int slice, int ks, int buf) {
-    const char* cur = lds + ((p0 + slice) & 1) * kStageBytes;
-    const int co = (((ks * 2) + (lane >> 5)) ^ sw) * 16;
-    read_a(cur, ks, co, buf, 0);
-    read_b(cur, co, buf, 0);
-    read_b(cur, co, buf, 1);
-#pragma unroll
-    for (int i = 1; i < 4; ++i) read_a(cur, ks, co, buf, i);
-  };
-  auto mfma = [&](int buf, int lo, int hi) {
-#pragma unroll
-    for (int q = lo; q < hi; ++q) {
-      const int i = q >> 1, j = q & 1;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+  // K-contiguous fragment reads: row (l % 16) of a 16-row block, chunk
+  // 4 ks + l / 16 of the 8 per row
+  const int rowsel = lane & 15;
+  const int kq = lane >> 4;
+  const int sw = swz(rowsel);
+  const int a_off = (wm * 128 + rowsel) * kRowBytes;
+  const int b_off = kOpBytes + (wn * 128 + rowsel) * kRowBytes;
+  // transposed reads: lane s of group g points at K-row 8 g + s / 4 (+ 4 for
+  // the upper half) and columns 4 (s % 4) .. +3 of the 16-column block
+  const int t_row = 8 * kq + (rowsel >> 2);
+  const int t_x = swz_mn(t_row);                        // same for the upper half
+  const int t_chunk = wm * 16 + ((rowsel & 3) >> 1);    // + 2 i
+  const int t_byte = 8 * (rowsel & 1);
+  const LoadOffs la = load_offsets<A_MN>(A), lb = load_offsets<false>(B);
+  const uint32_t wave_off = (uint32_t)wave_id() * 8192;   // this wave's 8 KB of an operand slice
+
+  bf16x8 fa[kNB], fb[2][kNB];
+  short8v ft[kNB];   // A_MN: the two transposed halves of each A fragment
+  auto cur_of = [&](int slice) { return lds + ((p0 + slice) & 1) * kStageBytes; };
+  auto rd_a = [&](int slice, int ks, int i, int h) {   // h: transposed half (A_MN) or -1 for both
+    const char* cur = cur_of(slice);
+    if (A_MN) {
+      auto half = [&](int hh) {
+        const char* p = cur + (ks * 32 + 4 * hh + t_row) * (kTile * 2) + (((t_chunk + 2 * i) ^ t_x) << 4) + t_byte;
+        const short4v v = ds_read_tr(p);
+        if (hh == 0) ft[i].s0123 = v; else ft[i].s4567 = v;
+      };
+      if (h <= 0) half(0);
+      if (h != 0) half(1);
+    } else {
+      const int co = (((ks * 4) + kq) ^ sw) * 16;
+      fa[i] = *reinterpret_cast<const bf16x8*>(cur + a_off + i * 16 * kRowBytes + co);
     }
   };
-  constexpr int kReads = A_MN ? 10 : 6;   // LDS read instructions per step
+  auto rd_b = [&](int slice, int ks, int set, int j) {
+    const int co = (((ks * 4) + kq) ^ sw) * 16;
+    fb[set][j] = *reinterpret_cast<const bf16x8*>(cur_of(slice) + b_off + j * 16 * kRowBytes + co);
+  };
+  // MFMA q of a step; the tile's first step starts every block from zero (an
+  // inline-constant accumulator operand, so the 256 AGPRs need no clearing)
+  auto mf = [&](int set, int q, bool first = false) {
+    const int i = q / kNB, j = q % kNB;
+    const bf16x8 a = A_MN ? __builtin_bit_cast(bf16x8, ft[i]) : fa[i];
+    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fb[set][j], first ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[i][j],
+                                                      0, 0, 0);
+  };
+  // reads after MFMA q of a full step (step ks_next - 1 of `slice`): B of the
+  // next step early, A fragment i right after its last use
+  auto step_reads = [&](int slice, int ks_next, int q) {
+    if (q < 2 * kNB && (q & 1) == 0) rd_b(slice, ks_next, ks_next & 1, q / 2);
+    if ((q & 7) == 7) rd_a(slice, ks_next, q / 8, -1);
+  };
+  // reads after MFMA q (32..63) of the last step of a slice: slice + 1's first
+  // step; A fragment i is free after MFMA 8 i + 7 (A_MN halves one slot apart,
+  // both after MFMA 63 for the last)
+  auto tail_reads = [&](int slice, int q) {
+    if (q < 32 + 2 * kNB && (q & 1) == 0) rd_b(slice, 0, 0, (q - 32) / 2);
+    if (q >= 48 && q < 62) {
+      const int i = (q - 48) / 2;
+      if (A_MN) rd_a(slice, 0, i, (q - 48) & 1);
+      else if ((q & 1) == 0) rd_a(slice, 0, i, -1);
+    }
+    if (q == 63) rd_a(slice, 0, kNB - 1, -1);
+  };
 
-  if (!pipe.staged) {
-    const uint32_t first = base + p0 * kStageBytes;
-    if (A_MN) stage_mn(A, 0, first); else stage(A, 0, first);
-    stage(B, 0, first + kOpBytes);
+  // stream slice g of this tile (g >= nk: the next tile's slice g - nk)
+  auto exists = [&](int g) { return g < nk || (chain && g - nk < nk); };
+  auto load_slice = [&](int g) {
+    const uint32_t st = __builtin_amdgcn_readfirstlane(base + ((p0 + g) & 1) * kStageBytes + wave_off);
+    const bool own = g < nk;
+    const int k0 = (own ? g : g - nk) * kBK;
+    const void* ba = slice_base<A_MN>(own ? A.base : nA_base, A.ld, k0);
+    const void* bb = slice_base<false>(own ? B.base : nB_base, B.ld, k0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dma16(la.o[q], ba, st + q * 1024);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dma16(lb.o[q], bb, st + kOpBytes + q * 1024);
+  };
+
+  // prologue: slices 0 and 1 in flight, slice 0 published, its first reads
+  if (pipe.staged == 0) load_slice(0);
+  const bool pro1 = pipe.staged < 2 && exists(1);
+  if (pro1) load_slice(1);
+  if (pipe.staged == 0) {
+    if (pro1) wait_vm<16>(); else wait_vm<0>();
+    __syncthreads();
   }
-  wait_vm<0>();
-  __syncthreads();
-  read_frags(0, 0, 0);
-
-  constexpr int kSteps = kBK / 16;
-  constexpr int kLast = (kSteps - 1) & 1;   // register set of the last step
-  const bool chain = nextA != nullptr;
-  auto slice = [&](int kt, bool more) {
-    const uint32_t nxt = base + ((p0 + kt + 1) & 1) * kStageBytes;
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int ks = 0; ks < kSteps - 1; ++ks) {
-      __builtin_amdgcn_sched_barrier(0);
-      // the other slot was freed by the barrier of the previous slice
-      if (more && ks == 0) {
-        if (A_MN) stage_mn(A, (kt + 1) * kBK, nxt); else stage(A, (kt + 1) * kBK, nxt);
-      }
-      if (more && ks == 1) stage(B, (kt + 1) * kBK, nxt + kOpBytes);
-      if (!more && chain && ks == 0) {
-        if (A_MN) stage_mn(*nextA, 0, nxt); else stage(*nextA, 0, nxt);
-      }
-      if (!more && chain && ks == 1) stage(*nextB, 0, nxt + kOpBytes);
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(kt, ks + 1, (ks + 1) & 1);
-      mfma(ks & 1, 0, 8);
-      Pin<8, kReads, 0>::run();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    mfma(kLast, 0, 4);
-    __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) {
-      // this wave's loads of slice kt + 1 are done; the barrier publishes
-      // everybody's and certifies that slice kt has been read by all waves
-      wait_vm<0>();
-      __syncthreads();
-      read_frags(kt + 1, 0, kLast ^ 1);
-    }
-    __builtin_amdgcn_s_setprio(1);
-    mfma(kLast, 4, 8);
-    if (more) Pin<4, kReads, 0>::run();
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(0);
+  for (int j = 0; j < kNB; ++j) rd_b(0, 0, 0, j);
+#pragma unroll
+  for (int i = 0; i < kNB; ++i) rd_a(0, 0, i, -1);
+
+  // loads of stream slice k + 2 (into the slot of slice k, or the scratch row),
+  // every address part but the per-lane offsets in SGPRs
+  struct Issue {
+    const void* ba;
+    const void* bb;
+    uint32_t sta, stb, step;   // LDS targets of load 0 and the step between loads
+    bool scratch;
   };
-  for (int kt = 0; kt < nk - 1; ++kt) slice(kt, true);
-  slice(nk - 1, false);
+  auto plan = [&](int k) {
+    const int g2 = k + 2;
+    const bool own = g2 < nk;
+    const bool next = !own && chain && (g2 - nk) < nk;
+    const int k0 = own ? g2 * kBK : (next ? (g2 - nk) * kBK : 0);
+    Issue is;
+    is.ba = slice_base<A_MN>(next ? nA_base : A.base, A.ld, k0);
+    is.bb = slice_base<false>(next ? nB_base : B.base, B.ld, k0);
+    is.scratch = !(own || next);
+    const uint32_t st = base + ((p0 + k) & 1) * kStageBytes + wave_off;
+    is.sta = __builtin_amdgcn_readfirstlane(is.scratch ? scratch_row : st);
+    is.stb = __builtin_amdgcn_readfirstlane(is.scratch ? scratch_row : st + kOpBytes);
+    is.step = is.scratch ? 0u : 1024u;
+    return is;
+  };
+  auto load = [&](const Issue& is, int d) {
+    if (d < 8) dma16(la.o[d], is.ba, is.sta + d * is.step);
+    else dma16(lb.o[d - 8], is.bb, is.stb + (d - 8) * is.step);
+  };
+  // the 16 loads over `slots` >= 16 slots: load d follows slot d * slots / 16
+  auto loads_at = [&](const Issue& is, int t, int slots) {
+    const int d = (t * 16 + slots - 1) / slots;
+    if (d < 16 && (d * slots) / 16 == t) load(is, d);
+  };
+
+  // head of slice 0: its first step and the first half of its second
+  __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+  for (int q = 0; q < NM; ++q) {
+    mf(0, q, true);
+    step_reads(0, 1, q);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int q = 0; q < NM / 2; ++q) {
+    mf(1, q);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // iteration k: publish slice k + 1, finish slice k, then the head of k + 1
+  auto iter = [&](int k, auto last_c) {
+    constexpr bool last = decltype(last_c)::value;
+    const Issue is = plan(k);
+    wait_vm<0>();          // slice k + 1 (this wave's part) has landed
+    __syncthreads();       // ... everybody's; and every wave has issued its reads of slice k
+#pragma unroll
+    for (int t = 0; t < NM / 2; ++t) {
+      mf(1, NM / 2 + t);
+      if (!last) tail_reads(k + 1, NM / 2 + t);
+      // the last iteration loads only for a chained next tile (that tile
+      // awaits them): nothing may still be landing in LDS when the workgroup
+      // ends (its LDS then belongs to the next workgroup on the CU)
+      if (!last) loads_at(is, t, NM);
+      else if (!is.scratch) loads_at(is, t, NM / 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (!last) {
+#pragma unroll
+      for (int q = 0; q < NM; ++q) {
+        mf(0, q);
+        step_reads(k + 1, 1, q);
+        loads_at(is, NM / 2 + q, NM);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int q = 0; q < NM / 2; ++q) {
+        mf(1, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  for (int k = 0; k < nk - 1; ++k) iter(k, std::false_type{});
+  iter(nk - 1, std::true_type{});
+  __builtin_amdgcn_s_setprio(0);
   pipe.slot = (p0 + nk) & 1;
-  pipe.staged = chain;
-  __syncthreads();
+  pipe.staged = chain ? (nk >= 2 ? 2 : 1) : 0;
+  if (!chain) __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);   // the epilogue's accumulator reads stay after the loop
 }
 
-// Row (within the wave's 128 rows) held by register r of sub-block i.
-__device__ __forceinline__ int acc_row(int i, int r, int lane) {
-  return i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-}
+// Row (within the wave's 128) held by register r of block i.
+__device__ __forceinline__ int acc_row(int i, int r, int lane) { return i * 16 + 4 * (lane >> 4) + r; }
 
 // Running statistics of one token over the vocabulary rows seen so far, in
 // base-2 units: m2 = max z * log2(e), s1 = sum 2^(z log2e - m2),
@@ -378,6 +457,8 @@ __device__ __forceinline__ Stats merge_stats(Stats a, Stats b) {
 // logit is kept untempered (the merge scales it). W holds the V vocabulary
 // rows from global id voff on (a vocabulary shard; voff = 0 for the whole
 // table): a target is picked here only when it falls inside that range.
+// Lane l of wave (wm, wn) holds tokens wn * 128 + 16 j + l % 16 (j = 0..7)
+// and, of each, 32 vocabulary rows of the wave's 128.
 __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W,
     const int32_t* __restrict__ targets, int N, int H, int V, int voff, int S, int n_tt, int n_vt,
@@ -393,11 +474,11 @@ __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
   const int wn = wave >> 1;
   const int tok0 = tt * kTile;
 
-  int tgt[2];
-  Stats st[2];
+  int tgt[kNB];
+  Stats st[kNB];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int tok = tok0 + wn * 64 + j * 32 + (lane & 31);
+  for (int j = 0; j < kNB; ++j) {
+    const int tok = tok0 + wn * 128 + j * 16 + (lane & 15);
     const int t = tok < N ? targets[tok] : -1;
     tgt[j] = (t >= voff && t - voff < V) ? t - voff : -1;   // local row, or no hit
     st[j].m2 = kNegBig;
@@ -411,14 +492,13 @@ __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
   for (int vt = s; vt < n_vt; vt += S) {
     const int v0 = vt * kTile;
     const Operand oa{W + (int64_t)v0 * H, H, min(kTile, V - v0)};
-    f32x16 acc[4][2];
-    if (vt + S < n_vt) {
-      const int v1 = v0 + S * kTile;
-      const Operand na{W + (int64_t)v1 * H, H, min(kTile, V - v1)};
-      mma_tile<false>(oa, ob, H, lds, acc, pipe, &na, &ob);
-    } else {
-      mma_tile<false>(oa, ob, H, lds, acc, pipe);
-    }
+    // one call site (a runtime chain flag): two inlined copies of the core
+    // would merge 256 accumulator registers. Chained only into a tile of the
+    // same shape (the next one is not the ragged last tile, or both are).
+    const int v1 = v0 + S * kTile;
+    const bool more = vt + S < n_vt && min(kTile, V - v1) == oa.rows;
+    f32x4 acc[kNB][kNB];
+    mma_tile<false>(oa, ob, H, lds, acc, pipe, W + (int64_t)(more ? v1 : v0) * H, ob.base, more);
 
     const int vrow0 = v0 + wm * 128;
     // ragged last tile: rows past V take no part. Their logits are set to
@@ -426,34 +506,37 @@ __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
     // and their exponentials are zeroed outright: scaled by sc < 1 the
     // rounding error of kNegBig * sc alone would overflow exp2.
     const bool ragged = vrow0 + 128 > V;
-    if (ragged) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < kNB; ++j) {
+      float z[kNB][4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool live = vrow0 + acc_row(i, r, lane) < V;
+      for (int i = 0; i < kNB; ++i) {
+        pin_acc(acc[i][j]);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j][r] = live ? acc[i][j][r] : kNegBig;
-        }
-    }
+        for (int r = 0; r < 4; ++r) z[i][r] = acc[i][j][r];
+      }
+      if (ragged) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+        for (int i = 0; i < kNB; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) z[i][r] = (vrow0 + acc_row(i, r, lane) < V) ? z[i][r] : kNegBig;
+      }
       // target logit: one-hot select, only in waves whose rows hold a target
       const int tr = tgt[j] - vrow0;
       const bool hit = (tr >= 0) && (tr < 128);
       if (__any(hit)) {
         float zt = st[j].zt;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kNB; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) zt = (acc_row(i, r, lane) == tr) ? acc[i][j][r] : zt;
+          for (int r = 0; r < 4; ++r) zt = (acc_row(i, r, lane) == tr) ? z[i][r] : zt;
         st[j].zt = zt;
       }
-      float mx = acc[0][j][0];
+      float mx = z[0][0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kNB; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = nan_max(mx, acc[i][j][r]);
+        for (int r = 0; r < 4; ++r) mx = nan_max(mx, z[i][r]);
       const float mnew = nan_max(st[j].m2, mx * sc);   // sc > 0: max commutes with the scaling
       const float dm = st[j].m2 - mnew;
       const float alpha = fast_exp2(dm);
@@ -461,21 +544,21 @@ __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
       float s2 = alpha * (st[j].s2 + dm * st[j].s1);
       if (!ragged) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kNB; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float d = fmaf(acc[i][j][r], sc, -mnew);
+          for (int r = 0; r < 4; ++r) {
+            const float d = fmaf(z[i][r], sc, -mnew);
             const float e = fast_exp2(d);
             s1 += e;
             s2 = fmaf(e, d, s2);
           }
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kNB; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
+          for (int r = 0; r < 4; ++r) {
             const bool live = vrow0 + acc_row(i, r, lane) < V;
-            const float d = live ? fmaf(acc[i][j][r], sc, -mnew) : 0.0f;
+            const float d = live ? fmaf(z[i][r], sc, -mnew) : 0.0f;
             const float e = live ? fast_exp2(d) : 0.0f;
             s1 += e;
             s2 = fmaf(e, d, s2);
@@ -484,34 +567,39 @@ __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
       st[j].m2 = mnew;
       st[j].s1 = s1;
       st[j].s2 = s2;
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // lanes l and l+32 hold other rows of the same tokens
+  // lanes l, l ^ 16, l ^ 32, l ^ 48 hold other rows of the same tokens:
+  // merge in a fixed order (the lower lane group's record first)
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    Stats o;
-    o.m2 = __shfl_xor(st[j].m2, 32);
-    o.s1 = __shfl_xor(st[j].s1, 32);
-    o.s2 = __shfl_xor(st[j].s2, 32);
-    o.zt = __shfl_xor(st[j].zt, 32);
-    st[j] = (lane < 32) ? merge_stats(st[j], o) : merge_stats(o, st[j]);
+  for (int x = 16; x <= 32; x <<= 1) {
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) {
+      Stats o;
+      o.m2 = __shfl_xor(st[j].m2, x);
+      o.s1 = __shfl_xor(st[j].s1, x);
+      o.s2 = __shfl_xor(st[j].s2, x);
+      o.zt = __shfl_xor(st[j].zt, x);
+      st[j] = (lane & x) == 0 ? merge_stats(st[j], o) : merge_stats(o, st[j]);
+    }
   }
   // waves wm = 0 and wm = 1 hold the two vocabulary halves of the same tokens
   float4* xch = reinterpret_cast<float4*>(lds);
-  if (wm == 1 && lane < 32) {
+  if (wm == 1 && lane < 16) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      xch[(wn * 2 + j) * 32 + lane] = make_float4(st[j].m2, st[j].s1, st[j].s2, st[j].zt);
+    for (int j = 0; j < kNB; ++j)
+      xch[(wn * kNB + j) * 16 + lane] = make_float4(st[j].m2, st[j].s1, st[j].s2, st[j].zt);
   }
   __syncthreads();
-  if (wm == 0 && lane < 32) {
+  if (wm == 0 && lane < 16) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float4 q = xch[(wn * 2 + j) * 32 + lane];
+    for (int j = 0; j < kNB; ++j) {
+      const float4 q = xch[(wn * kNB + j) * 16 + lane];
       const Stats o{q.x, q.y, q.z, q.w};
       const Stats m = merge_stats(st[j], o);
-      const int tok = tok0 + wn * 64 + j * 32 + lane;
+      const int tok = tok0 + wn * 128 + j * 16 + lane;
       if (tok < N) part[(int64_t)s * part_ld + tok] = make_float4(m.m2, m.s1, m.s2, m.zt);
     }
   }
@@ -578,11 +666,11 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
   // per-token inputs, loaded before the K loop so their latency hides behind
   // it; indices are clamped so every load is unconditional (a conditional load
   // per value costs a full memory round trip each)
-  int t_in[2];
-  float l_in[2], e_in[2], gl_in[2], ge_in[2];
+  int t_in[kNB];
+  float l_in[kNB], e_in[kNB], gl_in[kNB], ge_in[kNB];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int tl = tl0 + wn * 64 + j * 32 + (lane & 31);
+  for (int j = 0; j < kNB; ++j) {
+    const int tl = tl0 + wn * 128 + j * 16 + (lane & 15);
     const int tok = t0 + min(tl, Ct - 1);
     t_in[j] = s.targets[tok];
     if (tl >= Ct) t_in[j] = -1;
@@ -594,114 +682,108 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
 
   const Operand oa{s.W + (int64_t)(v0 + vl0) * H, H, min(kTile, Vb - vl0)};
   const Operand ob{s.hidden + (int64_t)(t0 + tl0) * H, H, min(kTile, Ct - tl0)};
-  f32x16 acc[4][2];
+  f32x4 acc[kNB][kNB];
   Pipe pipe;
-  mma_tile<false>(oa, ob, H, lds, acc, pipe);
+  mma_tile<false>(oa, ob, H, lds, acc, pipe, oa.base, ob.base, false);
 
-  float nlseL[2], c0[2], c1[2], gl[2];
-  int tr[2];
-  bool live[2];
   const int vw0 = vl0 + wm * 128;   // block-local vocabulary row of this wave
+  const bool ragged = (vw0 + 128 > Vb);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < kNB; ++j) {
     const int t = t_in[j];
-    live[j] = (t >= 0) && (t < Vtot);
+    const bool live = (t >= 0) && (t < Vtot);
     // masked tokens: every input is replaced (selected, never multiplied), so
     // whatever their rows hold cannot reach dz
-    const float L = live[j] ? l_in[j] : 0.0f;
-    const float Hn = live[j] ? e_in[j] : 0.0f;
-    const float ga = live[j] ? gl_in[j] : 0.0f;
-    const float gb = live[j] ? ge_in[j] : 0.0f;
-    nlseL[j] = -L * kLog2e;
+    const float L = live ? l_in[j] : 0.0f;
+    const float Hn = live ? e_in[j] : 0.0f;
+    const float ga = live ? gl_in[j] : 0.0f;
+    const float gb = live ? ge_in[j] : 0.0f;
+    const float nlseL = -L * kLog2e;
     // dz = p * (c1 * d + c0) (+ g_l / T at the target), d = log2 p
-    c0[j] = -(ga + gb * Hn) * s.invT;
-    c1[j] = -(gb * kLn2) * s.invT;
-    gl[j] = ga * s.invT;
+    const float c0 = -(ga + gb * Hn) * s.invT;
+    const float c1 = -(gb * kLn2) * s.invT;
+    const float gl = ga * s.invT;
     // target row relative to this wave's rows (a target of another shard or
     // block lands outside [0, 128) or on rows the ragged mask zeroes)
-    tr[j] = live[j] ? (t - s.voff - v0 - vw0) : -1;
-  }
-  const bool any_dead = __any(!live[0] || !live[1]);
-  const bool ragged = (vw0 + 128 > Vb);
-
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int tl = tl0 + wn * 64 + j * 32 + (lane & 31);
-    const bool hit_any = __any(tr[j] >= 0 && tr[j] < 128);
+    const int tr = live ? (t - s.voff - v0 - vw0) : -1;
+    const bool hit_any = __any(tr >= 0 && tr < 128);
+    const bool any_dead = __any(!live);
+    const int tl = tl0 + wn * 128 + j * 16 + (lane & 15);
     uint16_t* row = s.z_dz + (int64_t)tl * s.ld_dz + vw0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kNB; ++i) {
+      pin_acc(acc[i][j]);
+      float v[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = g * 4 + q;
-          const float d = fmaf(acc[i][j][r], s.sc, nlseL[j]);
-          const float p = fast_exp2(d);
-          float x = p * fmaf(c1[j], d, c0[j]);
-          if (hit_any) x = (acc_row(i, r, lane) == tr[j]) ? x + gl[j] : x;
-          if (any_dead) x = live[j] ? x : 0.0f;
-          if (ragged) x = (vw0 + acc_row(i, r, lane) < Vb) ? x : 0.0f;
-          v[q] = x;
-        }
-        uint2 w;
-        w.x = pack_bf16x2(v[0], v[1]);
-        w.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(row + i * 32 + 8 * g + 4 * (lane >> 5)) = w;
+      for (int r = 0; r < 4; ++r) {
+        const float d = fmaf(acc[i][j][r], s.sc, nlseL);
+        const float p = fast_exp2(d);
+        float x = p * fmaf(c1, d, c0);
+        if (hit_any) x = (acc_row(i, r, lane) == tr) ? x + gl : x;
+        if (any_dead) x = live ? x : 0.0f;
+        if (ragged) x = (vw0 + acc_row(i, r, lane) < Vb) ? x : 0.0f;
+        v[r] = x;
       }
+      uint2 w;
+      w.x = pack_bf16x2(v[0], v[1]);
+      w.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(row + acc_row(i, 0, lane)) = w;
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Writes a wave's 128 x 64 accumulator block into a float32 matrix (row
-// r_base + acc_row(i, r, lane), column c_base + 32 j + lane % 32; rows at or
-// past `rows` and columns at or past `cols` are skipped), storing or adding.
-// Rows whose target is masked (`targets` given, id outside [0, Vtot)) are
-// stored as 0, or left unchanged when adding. The read-modify-write is
-// batched per 32-row sub-block: its loads (and target ids) are all in flight
-// before the first add; one load-add-store per element would wait out the
-// whole memory latency 128 times per lane.
+// Write one wave's 128 x 128 accumulator block of a gradient tile: element
+// (row, col) of out, row = r_base + acc_row(i, r, lane), col = c_base + 16 j
+// + lane % 16; rows at or past `rows` and columns at or past `cols` are
+// skipped. With `add` the block is added to what out holds. With `targets`,
+// row m belongs to token t_base + m and masked tokens' rows are stored as 0,
+// or left unchanged when adding. The read-modify-write is batched per 16-row
+// block: its loads (and target ids) are all in flight before the first add;
+// one load-add-store per element would wait out the whole memory latency for
+// each.
 __device__ __forceinline__ void write_acc(float* __restrict__ out, int64_t ld, int r_base, int rows,
                                           int c_base, int cols, bool add, const int32_t* __restrict__ targets,
-                                          int t_base, int Vtot, const f32x16 (&acc)[4][2]) {
+                                          int t_base, int Vtot, f32x4 (&acc)[kNB][kNB]) {
   const int lane = threadIdx.x & 63;
-  bool col_ok[2];
-  int col[2];   // clamped into range, so every load below is unconditional
+  bool col_ok[kNB];
+  int col[kNB];   // clamped into range, so every load below is unconditional
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = c_base + j * 32 + (lane & 31);
+  for (int j = 0; j < kNB; ++j) {
+    const int c = c_base + j * 16 + (lane & 15);
     col_ok[j] = c < cols;
     col[j] = col_ok[j] ? c : cols - 1;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float old[16][2];
-    bool row_ok[16], live[16];
-    int row[16];
+  for (int i = 0; i < kNB; ++i) {
+    float old[4][kNB];
+    bool row_ok[4], live[4];
+    int row[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < 4; ++r) {
       const int m = r_base + acc_row(i, r, lane);
       row_ok[r] = m < rows;
       row[r] = row_ok[r] ? m : rows - 1;
       live[r] = true;
     }
     if (targets != nullptr) {
-      int t[16];
+      int t[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) t[r] = targets[t_base + row[r]];
+      for (int r = 0; r < 4; ++r) t[r] = targets[t_base + row[r]];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) live[r] = (t[r] >= 0) && (t[r] < Vtot);
+      for (int r = 0; r < 4; ++r) live[r] = (t[r] >= 0) && (t[r] < Vtot);
     }
     if (add) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) old[r][j] = out[(int64_t)row[r] * ld + col[j]];
+        for (int j = 0; j < kNB; ++j) old[r][j] = out[(int64_t)row[r] * ld + col[j]];
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int j = 0; j < kNB; ++j) {
+      pin_acc(acc[i][j]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int r = 0; r < 4; ++r) {
         if (!(row_ok[r] && col_ok[j])) continue;
         float* p = out + (int64_t)row[r] * ld + col[j];
         if (add) {
@@ -711,6 +793,7 @@ __device__ __forceinline__ void write_acc(float* __restrict__ out, int64_t ld, i
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -727,10 +810,10 @@ __device__ __forceinline__ void dw_tile(const BwdStep& s, int vid, char* lds) {
   const int H = s.H;
   const Operand oa{s.g_dz + m0, s.ld_dz, kTile};
   const Operand ob{s.ht + (int64_t)h0 * s.ld_ht + s.g_t0, s.ld_ht, kTile};
-  f32x16 acc[4][2];
+  f32x4 acc[kNB][kNB];
   Pipe pipe;
-  mma_tile<true>(oa, ob, (s.g_Ct + kBK - 1) / kBK * kBK, lds, acc, pipe);
-  write_acc(s.dW + (int64_t)s.g_v0 * H, H, m0 + wm * 128, s.g_Vb, h0 + wn * 64, H, s.g_acc_dW != 0,
+  mma_tile<true>(oa, ob, (s.g_Ct + kBK - 1) / kBK * kBK, lds, acc, pipe, oa.base, ob.base, false);
+  write_acc(s.dW + (int64_t)s.g_v0 * H, H, m0 + wm * 128, s.g_Vb, h0 + wn * 128, H, s.g_acc_dW != 0,
             nullptr, 0, 0, acc);
 }
 
@@ -747,10 +830,10 @@ __device__ __forceinline__ void dh_tile(const BwdStep& s, int vid, char* lds) {
   const int H = s.H;
   const Operand oa{s.g_dz + (int64_t)m0 * s.ld_dz, s.ld_dz, kTile};
   const Operand ob{s.Wt + (int64_t)h0 * s.ld_wt + s.g_v0, s.ld_wt, kTile};
-  f32x16 acc[4][2];
+  f32x4 acc[kNB][kNB];
   Pipe pipe;
-  mma_tile<false>(oa, ob, (s.g_Vb + kBK - 1) / kBK * kBK, lds, acc, pipe);
-  write_acc(s.dh + (int64_t)s.g_t0 * H, H, m0 + wm * 128, s.g_Ct, h0 + wn * 64, H, s.g_acc_dh != 0,
+  mma_tile<false>(oa, ob, (s.g_Vb + kBK - 1) / kBK * kBK, lds, acc, pipe, oa.base, ob.base, false);
+  write_acc(s.dh + (int64_t)s.g_t0 * H, H, m0 + wm * 128, s.g_Ct, h0 + wn * 128, H, s.g_acc_dh != 0,
             s.targets, s.g_t0, s.Vtot, acc);
 }
 
@@ -881,13 +964,13 @@ hipError_t launch_merge(const float* partials, int P, int64_t N, const int32_t* 
 }
 
 hipError_t launch_bwd_step(const BwdStep& st, hipStream_t stream) {
-  const int n_g = st.n_dw + st.n_dh;
   const int n_z = st.z_ntt * st.z_nvt;
   int per = 0;
   for (int x = 0; x < 8; ++x)
     per = max(per, ((x + 1) * st.n_dw / 8 - x * st.n_dw / 8) + ((x + 1) * st.n_dh / 8 - x * st.n_dh / 8) +
                        ((x + 1) * n_z / 8 - x * n_z / 8));
   if (per == 0) return hipSuccess;
+  const int n_g = st.n_dw + st.n_dh;
   const double H = (double)st.H;
   const double gc = (double)st.g_Ct, gv = (double)st.g_Vb;
   const double zc = (double)st.z_Ct, zv = (double)st.z_Vb;

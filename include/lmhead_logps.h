@@ -88,7 +88,7 @@ extern "C" {
 #define LMH_ERR_CHUNK (-3)       /* chunk_size <= 0 */
 #define LMH_ERR_WORKSPACE (-4)   /* workspace smaller than the queried size */
 #define LMH_ERR_ARGS (-5)        /* g_ent given without entropy; bad temperature */
-#define LMH_ERR_UNSUPPORTED (-6) /* H % 64 != 0, or a misaligned pointer */
+#define LMH_ERR_UNSUPPORTED (-6) /* H % 64 != 0, a misaligned pointer, or a backward with N or V > 2^23 - 256 */
 #define LMH_ERR_HIP (-7)         /* a HIP call or kernel launch failed */
 
 /*
@@ -96,7 +96,10 @@ extern "C" {
  * forward only; with_backward != 0 sizes a workspace that serves both the
  * forward and the backward (one buffer may be reused for both calls when
  * they run in stream order). Pure host computation, no device call.
- * Errors: LMH_ERR_NULL (bytes_out), LMH_ERR_SHAPE, LMH_ERR_CHUNK.
+ * Errors: LMH_ERR_NULL (bytes_out), LMH_ERR_SHAPE, LMH_ERR_CHUNK,
+ * LMH_ERR_UNSUPPORTED (with_backward and N or V above 2^23 - 256: the
+ * backward addresses 256-row tiles of its transposed operands with 32-bit
+ * offsets).
  */
 int lmhead_logps_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t chunk_size,
                                  int with_backward, size_t* bytes_out);
@@ -136,7 +139,8 @@ int lmhead_logps_fwd(const uint16_t* hidden, const uint16_t* W, const int32_t* t
  *   dW       f32 [V, H]    out, overwritten (not accumulated into)
  *   workspace: at least lmhead_logps_workspace_bytes(..., 1) bytes.
  * Errors: LMH_ERR_NULL, LMH_ERR_SHAPE, LMH_ERR_CHUNK, LMH_ERR_WORKSPACE,
- * LMH_ERR_ARGS (g_ent without entropy), LMH_ERR_UNSUPPORTED, LMH_ERR_HIP.
+ * LMH_ERR_ARGS (g_ent without entropy), LMH_ERR_UNSUPPORTED (including N or V
+ * above 2^23 - 256), LMH_ERR_HIP.
  * N = 0 writes dW = 0 and returns LMH_OK.
  */
 int lmhead_logps_bwd(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,

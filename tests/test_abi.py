@@ -115,6 +115,21 @@ def test_temperature_errors(call):
     assert call(0.7, workspace_bytes=0) == -4        # valid temperature: fails on the workspace next
 
 
+def test_backward_size_limit():
+    # 256-row tiles of the transposed operands are addressed with 32-bit byte
+    # offsets: the backward (and its workspace query) refuses N or V whose
+    # multiple of 256 reaches 2^23
+    lim = 1 << 23
+    assert _bwd(N=lim - 256, workspace_bytes=0) == -4        # within the limit: only the workspace is short
+    assert _bwd(N=lim - 255) == -6
+    assert _bwd(V=lim) == -6
+    b = nat.raw_workspace_bytes(lim - 256, 128, 300, 16, True)
+    assert b > 0
+    with pytest.raises(nat.LmheadError):
+        nat.raw_workspace_bytes(64, 128, lim - 255, 16, True)
+    assert nat.raw_workspace_bytes(64, 128, lim - 255, 16, False) > 0   # the forward has no such limit
+
+
 def test_backward_ex_flags():
     """lmhead_logps_bwd_ex accepts only its two accumulate bits."""
     a = dict(hidden=FAKE, W=FAKE, targets=FAKE, N=64, H=128, V=300, chunk_size=16, temperature=1.0,
