@@ -206,13 +206,15 @@ __device__ __forceinline__ short4v ds_read_tr(const char* p) {
 // A fragment i serves MFMAs 8 i .. 8 i + 7, B fragment j every eighth).
 // Schedule, in 16-cycle MFMA slots:
 //  * B fragments are double buffered: those of step s + 1 are read one every
-//    other MFMA at the start of step s. A fragments are single buffered:
+//    4 MFMAs in the first half of step s. A fragments are single buffered:
 //    fragment i of step s + 1 is read right after its last MFMA of step s,
 //    57 MFMAs ahead of its first use (this frees 32 VGPRs);
-//  * the loads of slice k + 2 go into the LDS slot slice k frees, one every
-//    4 MFMAs over the first 64 slots after the barrier that frees it: a burst
-//    of loads stalls the wave's issue, and with one wave per SIMD nothing
-//    else feeds the matrix pipe meanwhile;
+//  * the loads of slice k + 2 go into the LDS slot slice k frees, spread
+//    evenly over the first SPAN of the 128 slots after the barrier that frees
+//    it: a burst of loads stalls the wave's issue, and with one wave per SIMD
+//    nothing else feeds the matrix pipe meanwhile, while loads issued late may
+//    not have landed by the next barrier (measured best: 96 for the forward's
+//    chained walk, 64 for the backward's single tiles);
 //  * that barrier, which also publishes slice k + 1, sits halfway through the
 //    last step of slice k; the reads of slice k + 1's first step follow it.
 // The loop body runs from that barrier to the next, so its back edge falls
@@ -233,7 +235,7 @@ struct Pipe {
   int staged = 0;   // slices of this tile already issued (slice 0 then also published)
 };
 
-template <bool A_MN>
+template <bool A_MN, int SPAN>
 __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int K, char* lds,
                                          f32x4 (&acc)[kNB][kNB], Pipe& pipe, const uint16_t* nA_base,
                                          const uint16_t* nB_base, bool chain) {
@@ -295,7 +297,7 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
   // reads after MFMA q of a full step (step ks_next - 1 of `slice`): B of the
   // next step early, A fragment i right after its last use
   auto step_reads = [&](int slice, int ks_next, int q) {
-    if (q < 2 * kNB && (q & 1) == 0) rd_b(slice, ks_next, ks_next & 1, q / 2);
+    if (q < 4 * kNB && (q & 3) == 0) rd_b(slice, ks_next, ks_next & 1, q / 4);
     if ((q & 7) == 7) rd_a(slice, ks_next, q / 8, -1);
   };
   // reads after MFMA q (32..63) of the last step of a slice: slice + 1's first
@@ -365,7 +367,7 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
     if (d < 8) dma16(la.o[d], is.ba, is.sta + d * is.step);
     else dma16(lb.o[d - 8], is.bb, is.stb + (d - 8) * is.step);
   };
-  // the 16 loads over `slots` >= 16 slots: load d follows slot d * slots / 16
+  // the 16 loads over 16 <= `slots` <= 128 slots: load d follows slot d * slots / 16
   auto loads_at = [&](const Issue& is, int t, int slots) {
     const int d = (t * 16 + slots - 1) / slots;
     if (d < 16 && (d * slots) / 16 == t) load(is, d);
@@ -397,7 +399,7 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
       // the last iteration loads only for a chained next tile (that tile
       // awaits them): nothing may still be landing in LDS when the workgroup
       // ends (its LDS then belongs to the next workgroup on the CU)
-      if (!last) loads_at(is, t, NM);
+      if (!last) loads_at(is, t, SPAN);
       else if (!is.scratch) loads_at(is, t, NM / 2);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -406,12 +408,13 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
       for (int q = 0; q < NM; ++q) {
         mf(0, q);
         step_reads(k + 1, 1, q);
-        loads_at(is, NM / 2 + q, NM);
+        loads_at(is, NM / 2 + q, SPAN);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int q = 0; q < NM / 2; ++q) {
         mf(1, q);
+        loads_at(is, NM / 2 + NM + q, SPAN);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -498,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void fwd_stats_kernel(
     const int v1 = v0 + S * kTile;
     const bool more = vt + S < n_vt && min(kTile, V - v1) == oa.rows;
     f32x4 acc[kNB][kNB];
-    mma_tile<false>(oa, ob, H, lds, acc, pipe, W + (int64_t)(more ? v1 : v0) * H, ob.base, more);
+    mma_tile<false, 96>(oa, ob, H, lds, acc, pipe, W + (int64_t)(more ? v1 : v0) * H, ob.base, more);
 
     const int vrow0 = v0 + wm * 128;
     // ragged last tile: rows past V take no part. Their logits are set to
@@ -684,7 +687,7 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
   const Operand ob{s.hidden + (int64_t)(t0 + tl0) * H, H, min(kTile, Ct - tl0)};
   f32x4 acc[kNB][kNB];
   Pipe pipe;
-  mma_tile<false>(oa, ob, H, lds, acc, pipe, oa.base, ob.base, false);
+  mma_tile<false, 64>(oa, ob, H, lds, acc, pipe, oa.base, ob.base, false);
 
   const int vw0 = vl0 + wm * 128;   // block-local vocabulary row of this wave
   const bool ragged = (vw0 + 128 > Vb);
@@ -812,7 +815,7 @@ __device__ __forceinline__ void dw_tile(const BwdStep& s, int vid, char* lds) {
   const Operand ob{s.ht + (int64_t)h0 * s.ld_ht + s.g_t0, s.ld_ht, kTile};
   f32x4 acc[kNB][kNB];
   Pipe pipe;
-  mma_tile<true>(oa, ob, (s.g_Ct + kBK - 1) / kBK * kBK, lds, acc, pipe, oa.base, ob.base, false);
+  mma_tile<true, 64>(oa, ob, (s.g_Ct + kBK - 1) / kBK * kBK, lds, acc, pipe, oa.base, ob.base, false);
   write_acc(s.dW + (int64_t)s.g_v0 * H, H, m0 + wm * 128, s.g_Vb, h0 + wn * 128, H, s.g_acc_dW != 0,
             nullptr, 0, 0, acc);
 }
@@ -832,7 +835,7 @@ __device__ __forceinline__ void dh_tile(const BwdStep& s, int vid, char* lds) {
   const Operand ob{s.Wt + (int64_t)h0 * s.ld_wt + s.g_v0, s.ld_wt, kTile};
   f32x4 acc[kNB][kNB];
   Pipe pipe;
-  mma_tile<false>(oa, ob, (s.g_Vb + kBK - 1) / kBK * kBK, lds, acc, pipe, oa.base, ob.base, false);
+  mma_tile<false, 64>(oa, ob, (s.g_Vb + kBK - 1) / kBK * kBK, lds, acc, pipe, oa.base, ob.base, false);
   write_acc(s.dh + (int64_t)s.g_t0 * H, H, m0 + wm * 128, s.g_Ct, h0 + wn * 128, H, s.g_acc_dh != 0,
             s.targets, s.g_t0, s.Vtot, acc);
 }
