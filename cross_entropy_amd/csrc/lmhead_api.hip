@@ -67,9 +67,10 @@ FwdPlan plan_forward(int64_t N, int64_t H, int64_t V) {
 BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, int64_t chunk_size) {
   const int64_t T = kTileRows;
   N = std::max<int64_t>(N, 1);
-  // elements of one dz block (two bf16 buffers, 4 bytes per element in all):
-  // at most chunk_size * V, and at least one 256 x 256 tile.
-  const double budget = std::max<double>((double)chunk_size * (double)V, (double)(T * T));
+  // elements of one dz buffer, stride padding included (two bf16 buffers, 4
+  // bytes per element in all): at most chunk_size * V, and at least one
+  // 256 x 256 tile.
+  const double budget = std::max<double>((double)chunk_size * (double)V, (double)(T * spread_ld(T)));
   const int64_t n_pad = round_up(N, T);
   const int64_t v_pad = round_up(V, T);
   // model: the MFMA work is fixed; what the block shape changes is the f32
@@ -80,7 +81,8 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, int64_t chunk_size) {
   BwdPlan best;
   double best_t = 1e300;
   for (int64_t ct = T; ct <= n_pad; ct += T) {
-    int64_t vb = (int64_t)(budget / (double)ct) / T * T;
+    // spread_ld(vb) = vb + 64 for vb a multiple of 256
+    int64_t vb = ((int64_t)(budget / (double)ct) - 64) / T * T;
     vb = std::min(vb, v_pad);
     if (vb < T) break;
     const int64_t n_tb = ceil_div(N, ct);
@@ -100,11 +102,14 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, int64_t chunk_size) {
   best.N_pad = round_up(N, T);
   best.V_pad = round_up(V, T);
   best.H_pad = round_up(H, T);
-  const size_t one = (size_t)round_up(best.Ct * best.Vb * 2, 256);
+  best.ld_dz = spread_ld(best.Vb);
+  best.ld_wt = spread_ld(best.V_pad);
+  best.ld_ht = spread_ld(best.N_pad);
+  const size_t one = (size_t)round_up(best.Ct * best.ld_dz * 2, 256);
   best.off_dz1 = one;
   best.off_wt = 2 * one;
-  best.off_ht = best.off_wt + (size_t)round_up(best.H_pad * best.V_pad * 2, 256);
-  best.bytes = best.off_ht + (size_t)round_up(best.H_pad * best.N_pad * 2, 256);
+  best.off_ht = best.off_wt + (size_t)round_up(best.H_pad * best.ld_wt * 2, 256);
+  best.bytes = best.off_ht + (size_t)round_up(best.H_pad * best.ld_ht * 2, 256);
   return best;
 }
 
@@ -328,9 +333,9 @@ int bwd_impl(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, 
   uint16_t* dzbuf[2] = {reinterpret_cast<uint16_t*>(ws), reinterpret_cast<uint16_t*>(ws + p.off_dz1)};
   uint16_t* Wt = reinterpret_cast<uint16_t*>(ws + p.off_wt);
   uint16_t* ht = reinterpret_cast<uint16_t*>(ws + p.off_ht);
-  hipError_t te = lmh::launch_transpose(W, H, V, H, p.V_pad, p.H_pad, nullptr, V, Wt, p.V_pad, s);
+  hipError_t te = lmh::launch_transpose(W, H, V, H, p.V_pad, p.H_pad, nullptr, V, Wt, p.ld_wt, s);
   if (te == hipSuccess)
-    te = lmh::launch_transpose(hidden, H, N, H, p.N_pad, p.H_pad, targets, Vtot, ht, p.N_pad, s);
+    te = lmh::launch_transpose(hidden, H, N, H, p.N_pad, p.H_pad, targets, Vtot, ht, p.ld_ht, s);
   if (te != hipSuccess) return fail(LMH_ERR_HIP, "bwd: launch failed: %s", hipGetErrorString(te));
 
   lmh::BwdStep st{};
@@ -349,12 +354,12 @@ int bwd_impl(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, 
   st.sc = temper_scale(temperature);
   st.invT = inv_temperature(temperature);
   st.ht = ht;
-  st.ld_ht = p.N_pad;
+  st.ld_ht = p.ld_ht;
   st.Wt = Wt;
-  st.ld_wt = p.V_pad;
+  st.ld_wt = p.ld_wt;
   st.dh = dh;
   st.dW = dW;
-  st.ld_dz = p.Vb;
+  st.ld_dz = p.ld_dz;
   st.n_ht = (int)lmh::ceil_div(H, lmh::kTileRows);
   // blocks in a fixed order (token blocks outer, vocabulary blocks inner);
   // launch j forms block j's cotangent and runs block j-1's GEMMs

@@ -189,21 +189,29 @@ def _pad(x, m=256):
     return (x + m - 1) // m * m
 
 
+def _spread(x):
+    """Row stride of the backward's bf16 operands: a multiple of 64 elements
+    with an odd quotient (rows strided by a large power of two crowd onto few
+    memory channels)."""
+    return (((x + 63) // 64) | 1) * 64
+
+
 def _operand_copies(N, H, V):
-    """bf16 transposes of W and hidden held by the backward (input-sized)."""
-    return 2 * _pad(H) * (_pad(V) + _pad(max(N, 1)))
+    """bf16 transposes of W and hidden held by the backward (input-sized,
+    rows padded to the spread stride)."""
+    return 2 * _pad(H) * (_spread(_pad(V)) + _spread(_pad(max(N, 1))))
 
 
 @pytest.mark.parametrize("N,H,V,C", SHAPES)
 def test_backward_transient_within_one_f32_chunk_of_logits(N, H, V, C):
     """The backward's [tokens, vocab]-shaped transient (the cotangent block,
-    held twice in bf16) stays within one float32 [chunk_size, V] tensor (at
-    least one 256 x 256 tile); the rest of the workspace is the input-sized
-    transposes of W and hidden. The forward's workspace is O(N), independent
-    of V."""
+    held twice in bf16, its row padding included) stays within one float32
+    [chunk_size, V] tensor (at least one 256 x 256 tile with its padded row
+    stride); the rest of the workspace is the input-sized transposes of W and
+    hidden. The forward's workspace is O(N), independent of V."""
     b = nat.raw_workspace_bytes(N, H, V, C, True)
     f = nat.raw_workspace_bytes(N, H, V, C, False)
-    assert b <= max(C * V * 4, 256 * 256 * 4) + _operand_copies(N, H, V) + max(f, 1024)
+    assert b <= max(C * V * 4, 256 * _spread(256) * 4) + _operand_copies(N, H, V) + max(f, 1024)
     assert f <= 16 * 128 * max(64, (N + 63) // 64 * 64) + 256
 
 
