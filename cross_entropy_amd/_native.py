@@ -202,7 +202,7 @@ def raw_bwd_shard(hidden, W_shard, targets, N, H, V_shard, vocab_offset, V_total
 
 
 TRACE_KERNELS = ("fwd_stats_kernel", "fwd_merge_kernel", "bwd_step_kernel", "transpose_kernel",
-                 "fill_zero_kernel")
+                 "fill_zero_kernel", "pad_rows_kernel")
 
 
 def trace_enable(on: bool) -> None:

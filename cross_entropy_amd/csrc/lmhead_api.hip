@@ -15,8 +15,9 @@
 //    per element, stay within one float32 [chunk_size, V] tensor, the
 //    transient the pages' chunked head holds per chunk. Within that bound the
 //    block shape is chosen to cut the dh / dW accumulation traffic and launch
-//    count. The workspace also holds bf16 transposes of W and of the hidden
-//    states (input-sized) for the K-contiguous operands of the GEMMs.
+//    count. The workspace also holds a bf16 transpose of the hidden states
+//    (input-sized; the dW GEMM's K-contiguous operand) and W's last V % 64
+//    rows padded to 64 (the dh GEMM reads W as it lies, 64 rows at a time).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -103,13 +104,12 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, int64_t chunk_size) {
   best.V_pad = round_up(V, T);
   best.H_pad = round_up(H, T);
   best.ld_dz = spread_ld(best.Vb);
-  best.ld_wt = spread_ld(best.V_pad);
   best.ld_ht = spread_ld(best.N_pad);
   const size_t one = (size_t)round_up(best.Ct * best.ld_dz * 2, 256);
   best.off_dz1 = one;
-  best.off_wt = 2 * one;
-  best.off_ht = best.off_wt + (size_t)round_up(best.H_pad * best.ld_wt * 2, 256);
-  best.bytes = best.off_ht + (size_t)round_up(best.H_pad * best.ld_ht * 2, 256);
+  best.off_ht = 2 * one;
+  best.off_tail = best.off_ht + (size_t)round_up(best.H_pad * best.ld_ht * 2, 256);
+  best.bytes = best.off_tail + (size_t)round_up(64 * H * 2, 256);
   return best;
 }
 
@@ -147,9 +147,10 @@ int check_shape(int64_t N, int64_t H, int64_t V, int64_t chunk_size) {
   return LMH_OK;
 }
 
-// The backward's GEMMs read 256-row tiles of the transposed W and hidden
-// states (row strides V_pad and N_pad elements) through 32-bit byte offsets
-// from the tile's base: 256 * stride * 2 bytes must stay below 2^32.
+// The backward's GEMMs read 256-row tiles of the cotangent block and of the
+// transposed hidden states (row strides up to V_pad and N_pad elements)
+// through 32-bit byte offsets from the tile's base: 256 * stride * 2 bytes
+// must stay below 2^32.
 int check_backward_size(int64_t N, int64_t V) {
   const int64_t lim = int64_t(1) << 23;
   if (lmh::round_up(std::max<int64_t>(N, 1), lmh::kTileRows) >= lim || lmh::round_up(V, lmh::kTileRows) >= lim)
@@ -323,19 +324,19 @@ int bwd_impl(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, 
   }
   if (!hidden || !W || !targets || !lse || !dh || !workspace)
     return fail(LMH_ERR_NULL, "bwd: hidden, W, targets, lse, dh, dW and workspace must be non-NULL");
-  if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(workspace, 16) || !aligned(dh, 4) ||
+  if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(workspace, 16) || !aligned(dh, 16) ||
       !aligned(dW, 4))
-    return fail(LMH_ERR_UNSUPPORTED, "bwd: hidden, W and workspace need 16-byte alignment");
+    return fail(LMH_ERR_UNSUPPORTED, "bwd: hidden, W, dh and workspace need 16-byte alignment");
   const lmh::BwdPlan p = lmh::plan_backward(N, H, V, chunk_size);
   if (workspace_bytes < p.bytes)
     return fail(LMH_ERR_WORKSPACE, "bwd: workspace of %zu bytes, %zu needed", workspace_bytes, p.bytes);
   char* ws = static_cast<char*>(workspace);
   uint16_t* dzbuf[2] = {reinterpret_cast<uint16_t*>(ws), reinterpret_cast<uint16_t*>(ws + p.off_dz1)};
-  uint16_t* Wt = reinterpret_cast<uint16_t*>(ws + p.off_wt);
   uint16_t* ht = reinterpret_cast<uint16_t*>(ws + p.off_ht);
-  hipError_t te = lmh::launch_transpose(W, H, V, H, p.V_pad, p.H_pad, nullptr, V, Wt, p.ld_wt, s);
-  if (te == hipSuccess)
-    te = lmh::launch_transpose(hidden, H, N, H, p.N_pad, p.H_pad, targets, Vtot, ht, p.ld_ht, s);
+  uint16_t* W_tail = reinterpret_cast<uint16_t*>(ws + p.off_tail);
+  const int64_t v_tail = V / 64 * 64;
+  hipError_t te = lmh::launch_transpose(hidden, H, N, H, p.N_pad, p.H_pad, targets, Vtot, ht, p.ld_ht, s);
+  if (te == hipSuccess && v_tail < V) te = lmh::launch_pad_rows(W + v_tail * H, V - v_tail, H, 64, W_tail, s);
   if (te != hipSuccess) return fail(LMH_ERR_HIP, "bwd: launch failed: %s", hipGetErrorString(te));
 
   lmh::BwdStep st{};
@@ -355,8 +356,8 @@ int bwd_impl(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, 
   st.invT = inv_temperature(temperature);
   st.ht = ht;
   st.ld_ht = p.ld_ht;
-  st.Wt = Wt;
-  st.ld_wt = p.ld_wt;
+  st.W_tail = v_tail < V ? W_tail : nullptr;
+  st.v_tail = (int)v_tail;
   st.dh = dh;
   st.dW = dW;
   st.ld_dz = p.ld_dz;

@@ -29,14 +29,15 @@ inline int64_t spread_ld(int64_t x) { return (((x + 63) / 64) | 1) * 64; }
 // Backward: the token x vocabulary plane is cut into blocks of at most
 // Ct x Vb; each block's cotangent is one bf16 buffer dz [Ct][ld_dz], double
 // buffered (4 bytes per element in all, like one float32 block, the stride
-// padding included). The workspace also holds W^T [H_pad][ld_wt] and
-// hidden^T [H_pad][ld_ht].
+// padding included). The workspace also holds hidden^T [H_pad][ld_ht]
+// (masked tokens zeroed) and W's last V % 64 rows zero-padded to 64 rows
+// [64][H] (the dh GEMM's last vocabulary slice).
 struct BwdPlan {
   int64_t Ct = 0, Vb = 0;      // block edges (tokens, vocabulary), multiples of 256
   int64_t n_tb = 0, n_vb = 0;  // blocks along tokens and vocabulary
   int64_t N_pad = 0, V_pad = 0, H_pad = 0;
-  int64_t ld_dz = 0, ld_wt = 0, ld_ht = 0;      // row strides (spread_ld)
-  size_t off_dz1 = 0, off_wt = 0, off_ht = 0;   // byte offsets in the workspace
+  int64_t ld_dz = 0, ld_ht = 0;                   // row strides (spread_ld)
+  size_t off_dz1 = 0, off_ht = 0, off_tail = 0;   // byte offsets in the workspace
   size_t bytes = 0;            // total
 };
 
@@ -77,8 +78,8 @@ struct BwdStep {
   float invT;   // 1 / T
   const uint16_t* ht;   // hidden^T [H_pad][N_pad], masked tokens zeroed
   int64_t ld_ht;
-  const uint16_t* Wt;   // W^T [H_pad][V_pad]
-  int64_t ld_wt;
+  const uint16_t* W_tail;   // W rows v_tail .. V-1 padded with zero rows to 64, or NULL if V % 64 == 0
+  int v_tail;               // V rounded down to a multiple of 64
   float* dh;
   float* dW;
   int64_t ld_dz;        // row stride of both dz buffers
@@ -92,7 +93,7 @@ struct BwdStep {
 };
 
 // Kernel ids of the tracing facility (lmhead_trace.hip).
-enum KernelId { kFwdStats = 0, kFwdMerge, kBwdStep, kTranspose, kFill, kNumKernels };
+enum KernelId { kFwdStats = 0, kFwdMerge, kBwdStep, kTranspose, kFill, kPadRows, kNumKernels };
 void trace_begin(hipStream_t stream);
 void trace_end(int kernel, hipStream_t stream, double flops, double bytes);
 
@@ -102,6 +103,8 @@ hipError_t launch_merge(const float* partials, int P, int64_t N, const int32_t* 
                         float invT, float* logp, float* entropy, float* lse, hipStream_t stream);
 hipError_t launch_bwd_step(const BwdStep& st, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+hipError_t launch_pad_rows(const uint16_t* in, int64_t R, int64_t C, int64_t R_pad, uint16_t* out,
+                           hipStream_t stream);
 hipError_t launch_transpose(const uint16_t* in, int64_t ld_in, int64_t R, int64_t C, int64_t R_pad,
                             int64_t C_pad, const int32_t* tgt, int64_t V, uint16_t* out,
                             int64_t ld_out, hipStream_t stream);

@@ -20,10 +20,10 @@
 // issues work (see mma_tile). K is staged through two 64-wide LDS slices
 // filled by direct-to-LDS loads (global_load_lds_dwordx4), so no VGPRs hold
 // staged data. Slice rows are 128 bytes with a 16-byte-chunk XOR swizzle,
-// which keeps the fragment reads free of bank conflicts. Operands stored
-// MN-contiguous are read with transposed LDS reads (the dW GEMM's cotangent)
-// or given to the core through transposed copies (W and hidden in the
-// backward).
+// which keeps the fragment reads free of bank conflicts. An A operand stored
+// MN-contiguous (W and the cotangent in the backward) is staged as it lies
+// and read with transposed LDS reads; the hidden states enter the dW GEMM
+// through a transposed copy.
 //
 // MFMA 16x16x32 register layout used throughout (wave64): lane l supplies
 // row (l % 16) of A and column (l % 16) of B with the 8 K values
@@ -105,12 +105,17 @@ __device__ __forceinline__ void pin_acc(f32x4& a) { asm volatile("" : "+a"(a)); 
 // (row, k) at base[row * ld + k], rows at or past `rows` are read as row
 // rows-1 (their results are discarded or masked by the epilogues), so every
 // load stays in bounds; an MN-contiguous operand holds element (m, k) at
-// base[k * ld + m]. Byte offsets within a tile stay below 2^32 (the host
-// bounds ld).
+// base[k * ld + m], columns m at or past `rows` (a multiple of 8) are read
+// as one of the last 8, and its slice at K offset tail_k (if any) is read
+// from `tail` (64 rows of stride ld) instead: a slice that would run past
+// the end of the matrix. Byte offsets within a tile stay below 2^32 (the
+// host bounds ld).
 struct Operand {
   const uint16_t* base;
   int64_t ld;
   int rows;
+  const uint16_t* tail = nullptr;
+  int tail_k = -1;
 };
 
 // XOR applied to the 16-byte chunk index of staged row r (8 chunks per row):
@@ -149,7 +154,7 @@ __device__ __forceinline__ void wait_vm() {
 //  K-contiguous: rows 64 w + 8 q .. +7; lane l fills physical chunk l % 8
 //    of row 64 w + 8 q + l / 8 with the logical chunk the swizzle puts there;
 //  MN-contiguous: K-rows 16 w + 2 q, +1; lane l fills physical chunk l % 32
-//    of K-row 16 w + 2 q + l / 32 likewise.
+//    of K-row 16 w + 2 q + l / 32 likewise (chunks past `rows` clamped).
 struct LoadOffs {
   uint32_t o[8];
 };
@@ -163,7 +168,7 @@ __device__ __forceinline__ LoadOffs load_offsets(const Operand& op) {
   for (int q = 0; q < 8; ++q) {
     if (MN) {
       const int r = wave * 16 + 2 * q + (lane >> 5);
-      const int c = (lane & 31) ^ swz_mn(r);
+      const int c = min((lane & 31) ^ swz_mn(r), ((op.rows + 7) >> 3) - 1);
       d.o[q] = (uint32_t)((int64_t)r * op.ld * 2) + (uint32_t)(c * 16);
     } else {
       const int r = wave * 64 + 8 * q + (lane >> 3);
@@ -175,11 +180,12 @@ __device__ __forceinline__ LoadOffs load_offsets(const Operand& op) {
   return d;
 }
 
-// Scalar base of a slice load: an operand starting at `base` (row stride
-// ld) at K offset k0, in SGPRs.
+// Scalar base of a slice load, in SGPRs: operand op's slice at K offset k0
+// (`own`), or that of the same-shaped operand starting at `base`.
 template <bool MN>
-__device__ __forceinline__ const void* slice_base(const uint16_t* base, int64_t ld, int k0) {
-  const char* b = reinterpret_cast<const char*>(base) + 2 * (MN ? (int64_t)k0 * ld : (int64_t)k0);
+__device__ __forceinline__ const void* slice_base(const Operand& op, const uint16_t* base, int k0, bool own) {
+  const char* b = reinterpret_cast<const char*>(base) + 2 * (MN ? (int64_t)k0 * op.ld : (int64_t)k0);
+  if (MN && own && k0 == op.tail_k) b = reinterpret_cast<const char*>(op.tail);
   const uint64_t bu = reinterpret_cast<uint64_t>(b);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bu);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bu >> 32));
@@ -319,8 +325,8 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
     const uint32_t st = __builtin_amdgcn_readfirstlane(base + ((p0 + g) & 1) * kStageBytes + wave_off);
     const bool own = g < nk;
     const int k0 = (own ? g : g - nk) * kBK;
-    const void* ba = slice_base<A_MN>(own ? A.base : nA_base, A.ld, k0);
-    const void* bb = slice_base<false>(own ? B.base : nB_base, B.ld, k0);
+    const void* ba = slice_base<A_MN>(A, own ? A.base : nA_base, k0, own);
+    const void* bb = slice_base<false>(B, own ? B.base : nB_base, k0, own);
 #pragma unroll
     for (int q = 0; q < 8; ++q) dma16(la.o[q], ba, st + q * 1024);
 #pragma unroll
@@ -354,8 +360,8 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
     const bool next = !own && chain && (g2 - nk) < nk;
     const int k0 = own ? g2 * kBK : (next ? (g2 - nk) * kBK : 0);
     Issue is;
-    is.ba = slice_base<A_MN>(next ? nA_base : A.base, A.ld, k0);
-    is.bb = slice_base<false>(next ? nB_base : B.base, B.ld, k0);
+    is.ba = slice_base<A_MN>(A, next ? nA_base : A.base, k0, !next);
+    is.bb = slice_base<false>(B, next ? nB_base : B.base, k0, !next);
     is.scratch = !(own || next);
     const uint32_t st = base + ((p0 + k) & 1) * kStageBytes + wave_off;
     is.sta = __builtin_amdgcn_readfirstlane(is.scratch ? scratch_row : st);
@@ -643,7 +649,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(
 // ---------------------------------------------------------------------------
 // Backward. The token x vocabulary plane is cut into blocks; each block's
 // cotangent is held as one bf16 buffer dz[token - t0][vocab - v0] and read
-// by both gradient GEMMs (the dW GEMM through transposed LDS reads). Launch
+// by both gradient GEMMs (the dW GEMM as its MN-contiguous operand). Launch
 // j of the backward carries the dh / dW tiles of block j - 1 (reading dz
 // buffer (j - 1) % 2) and the cotangent tiles of block j (writing buffer
 // j % 2): the short cotangent tiles fill the tail of the long GEMM tiles,
@@ -820,8 +826,59 @@ __device__ __forceinline__ void dw_tile(const BwdStep& s, int vid, char* lds) {
             nullptr, 0, 0, acc);
 }
 
-// dh tile: dh[t0 + m][n] (+)= sum_k dz[m][k] Wt[n][v0 + k] over the block's
-// vocabulary; masked token rows are written as 0 (left alone when adding).
+// Write one wave's 128 x 128 accumulator block transposed: element (row,
+// col) goes to out[col][row], row = r_base + acc_row(i, r, lane) (the 4
+// registers of a block are 4 consecutive rows: one 16-byte access), col =
+// c_base + 16 j + lane % 16. Rows at or past `rows` (a multiple of 16) and
+// columns at or past `cols` are skipped. With `add` the block is added to
+// what out holds. Column c belongs to token t_base + c: masked tokens'
+// columns are stored as 0, or left unchanged when adding. Batched per
+// column: one 64-bit address, 8 accesses at fixed offsets from it.
+__device__ __forceinline__ void write_acc_t(float* __restrict__ out, int64_t ld, int r_base, int rows,
+                                            int c_base, int cols, bool add, const int32_t* __restrict__ targets,
+                                            int t_base, int Vtot, f32x4 (&acc)[kNB][kNB]) {
+  const int lane = threadIdx.x & 63;
+  int col[kNB], tgt[kNB];
+#pragma unroll
+  for (int j = 0; j < kNB; ++j) {
+    const int c = c_base + j * 16 + (lane & 15);
+    col[j] = c < cols ? c : cols - 1;   // clamped, so the loads below are unconditional
+    tgt[j] = targets[t_base + col[j]];
+    if (c >= cols) tgt[j] = -2;         // not stored
+  }
+  // a wave with no row in range points its (unused) loads at row 0; the
+  // loads of blocks past `rows` reread block 0 (a select, not a branch: a
+  // branch per load makes the compiler copy the accumulators out)
+  const int r0 = (r_base < rows ? r_base : 0) + 4 * (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < kNB; ++j) {
+    const bool in = tgt[j] != -2;
+    const bool live = (tgt[j] >= 0) && (tgt[j] < Vtot);
+    f32x4* p = reinterpret_cast<f32x4*>(out + (int64_t)col[j] * ld + r0);
+    f32x4 old[kNB];
+    if (add) {
+#pragma unroll
+      for (int i = 0; i < kNB; ++i) old[i] = p[r_base + 16 * i < rows ? 4 * i : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) {
+      pin_acc(acc[i][j]);
+      if (!(r_base + 16 * i < rows) || !in) continue;
+      if (add) {
+        if (live) p[4 * i] = old[i] + acc[i][j];
+      } else {
+        p[4 * i] = live ? acc[i][j] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// dh tile, computed transposed: dh[t0 + m][n] (+)= sum_k W[v0 + k][n] dz[m][k]
+// over the block's vocabulary (A = W as it lies, MN-contiguous, B = the
+// cotangent rows); masked token rows are written as 0 (left alone when
+// adding). W's rows past V in the block's last slice are read from the
+// zero-padded copy of its last rows.
 __device__ __forceinline__ void dh_tile(const BwdStep& s, int vid, char* lds) {
   int mt, hb;
   raster(vid, s.n_dh / s.n_ht, s.n_ht, 4, mt, hb);
@@ -831,13 +888,15 @@ __device__ __forceinline__ void dh_tile(const BwdStep& s, int vid, char* lds) {
   const int m0 = mt * kTile;
   const int h0 = hb * kTile;
   const int H = s.H;
-  const Operand oa{s.g_dz + (int64_t)m0 * s.ld_dz, s.ld_dz, kTile};
-  const Operand ob{s.Wt + (int64_t)h0 * s.ld_wt + s.g_v0, s.ld_wt, kTile};
+  const int tail_k = s.W_tail != nullptr ? s.v_tail - s.g_v0 : -1;
+  const Operand oa{s.W + (int64_t)s.g_v0 * H + h0, H, min(kTile, H - h0),
+                   s.W_tail != nullptr ? s.W_tail + h0 : nullptr, tail_k};
+  const Operand ob{s.g_dz + (int64_t)m0 * s.ld_dz, s.ld_dz, kTile};
   f32x4 acc[kNB][kNB];
   Pipe pipe;
-  mma_tile<false, 64>(oa, ob, (s.g_Vb + kBK - 1) / kBK * kBK, lds, acc, pipe, oa.base, ob.base, false);
-  write_acc(s.dh + (int64_t)s.g_t0 * H, H, m0 + wm * 128, s.g_Ct, h0 + wn * 128, H, s.g_acc_dh != 0,
-            s.targets, s.g_t0, s.Vtot, acc);
+  mma_tile<true, 64>(oa, ob, (s.g_Vb + kBK - 1) / kBK * kBK, lds, acc, pipe, oa.base, ob.base, false);
+  write_acc_t(s.dh + (int64_t)s.g_t0 * H, H, h0 + wm * 128, H, m0 + wn * 128, s.g_Ct, s.g_acc_dh != 0,
+              s.targets, s.g_t0, s.Vtot, acc);
 }
 
 // One backward launch: each XCD (workgroups are dealt to the 8 XCDs
@@ -923,6 +982,20 @@ __global__ __launch_bounds__(256) void transpose_kernel(
   }
 }
 
+// Row copy with zero padding: out[r][c] = in[r][c] for r < R, 0 for
+// R <= r < R_pad (c < C, C % 8 == 0; both of row stride C). One 16-byte
+// chunk per thread.
+__global__ __launch_bounds__(256) void pad_rows_kernel(const uint16_t* __restrict__ in, int R, int C,
+                                                       int R_pad, uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int cpr = C / 8;
+  if (i >= (int64_t)R_pad * cpr) return;
+  const int r = (int)(i / cpr);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (r < R) v = reinterpret_cast<const uint4*>(in)[i];
+  reinterpret_cast<uint4*>(out)[i] = v;
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * 256;
@@ -1000,6 +1073,19 @@ hipError_t launch_transpose(const uint16_t* in, int64_t ld_in, int64_t R, int64_
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   trace_end(kTranspose, stream, 0.0, 2.0 * (double)R * C + 2.0 * (double)R_pad * C_pad);
+  return hipSuccess;
+}
+
+hipError_t launch_pad_rows(const uint16_t* in, int64_t R, int64_t C, int64_t R_pad, uint16_t* out,
+                           hipStream_t stream) {
+  const long long n = R_pad * (C / 8);
+  if (n <= 0) return hipSuccess;
+  trace_begin(stream);
+  hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, in, (int)R,
+                     (int)C, (int)R_pad, out);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  trace_end(kPadRows, stream, 0.0, 2.0 * (double)R * C + 2.0 * (double)R_pad * C);
   return hipSuccess;
 }
 

@@ -41,8 +41,8 @@
  *    holds at any time is at most one float32 [chunk_size, V] tensor in bytes
  *    (it is kept as two bf16 buffers of a block of tokens x vocabulary, the
  *    next block's formed while the current one's is used). The backward
- *    workspace also holds bf16
- *    transposes of W and of the hidden states (input-sized). The forward
+ *    workspace also holds a bf16 transpose of the hidden states
+ *    (input-sized) and a copy of W's last V % 64 rows. The forward
  *    holds no [tokens, vocab] transient at all. Per-token forward results do not depend on
  *    chunk_size; gradients depend on it only through float32 summation order.
  *  - Targets outside [0, V) (-1 included) mask the token: its logp, entropy
@@ -252,8 +252,9 @@ const char* lmhead_logps_version(void);
  *   1 fwd_merge_kernel  (split merge)
  *   2 bwd_step_kernel   (dh and dW GEMMs of one block + the logits recompute
  *                        and cotangent of the next block)
- *   3 transpose_kernel  (bf16 transposes of W and hidden)
+ *   3 transpose_kernel  (bf16 transpose of the hidden states)
  *   4 fill_zero_kernel
+ *   5 pad_rows_kernel   (W's last V % 64 rows, zero-padded to 64)
  * lmhead_logps_trace_enable(on) clears the totals and starts (on != 0) or
  * stops recording. lmhead_logps_trace_read(kernel, ...) waits for the
  * recorded launches to finish and returns, for that kernel, the launch

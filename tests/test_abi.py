@@ -83,6 +83,7 @@ def test_backward_null_args_alignment_and_workspace_errors():
     for k in ("hidden", "W", "targets", "lse", "dh", "workspace"):
         assert _bwd(**{k: 0}) == -1, k
     assert _bwd(hidden=MIS) == -6
+    assert _bwd(dh=FAKE + 4) == -6         # dh is written 16 bytes at a time
     need = nat.raw_workspace_bytes(64, 128, 300, 16, True)
     assert _bwd(workspace_bytes=need - 1) == -4
 
@@ -197,9 +198,10 @@ def _spread(x):
 
 
 def _operand_copies(N, H, V):
-    """bf16 transposes of W and hidden held by the backward (input-sized,
-    rows padded to the spread stride)."""
-    return 2 * _pad(H) * (_spread(_pad(V)) + _spread(_pad(max(N, 1))))
+    """Input-sized operand copies held by the backward: the bf16 transpose of
+    hidden (rows padded to the spread stride) and W's last V % 64 rows padded
+    to 64 rows."""
+    return 2 * _pad(H) * _spread(_pad(max(N, 1))) + _pad(64 * H * 2)
 
 
 @pytest.mark.parametrize("N,H,V,C", SHAPES)
@@ -207,8 +209,9 @@ def test_backward_transient_within_one_f32_chunk_of_logits(N, H, V, C):
     """The backward's [tokens, vocab]-shaped transient (the cotangent block,
     held twice in bf16, its row padding included) stays within one float32
     [chunk_size, V] tensor (at least one 256 x 256 tile with its padded row
-    stride); the rest of the workspace is the input-sized transposes of W and
-    hidden. The forward's workspace is O(N), independent of V."""
+    stride); the rest of the workspace is the input-sized transpose of hidden
+    and W's padded last rows. The forward's workspace is O(N), independent of
+    V."""
     b = nat.raw_workspace_bytes(N, H, V, C, True)
     f = nat.raw_workspace_bytes(N, H, V, C, False)
     assert b <= max(C * V * 4, 256 * _spread(256) * 4) + _operand_copies(N, H, V) + max(f, 1024)

@@ -161,7 +161,8 @@ def test_tracing_counts_launches():
     tr = _native.trace_read()
     _native.trace_enable(False)
     assert tr["fwd_stats_kernel"]["launches"] == 1 and tr["fwd_merge_kernel"]["launches"] == 1
-    assert tr["bwd_step_kernel"]["launches"] >= 2 and tr["transpose_kernel"]["launches"] == 2
+    assert tr["bwd_step_kernel"]["launches"] >= 2 and tr["transpose_kernel"]["launches"] == 1
+    assert tr["pad_rows_kernel"]["launches"] == 1   # 1000 % 64 != 0: W's last rows are padded
     assert abs(tr["fwd_stats_kernel"]["flops"] - 2.0 * 300 * 128 * 1000) < 1.0
     assert tr["fwd_stats_kernel"]["ms"] > 0.0
     _ = lm
