@@ -125,8 +125,12 @@ __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) &
 
 // MN-contiguous slice rows (64 K-rows of 256 m, 512 bytes each): chunk XOR by
 // 2 * (k % 4), so the 4 K-rows one 16-lane group of a transposed read visits
-// land on distinct bank groups.
-__device__ __forceinline__ int swz_mn(int k) { return 2 * (k & 3); }
+// land on distinct bank groups, and by 8 for K-rows with bit 3 set, so the
+// two 16-lane groups served together (32 lanes x 8 bytes per pass over the 64
+// banks), 8 K-rows apart, fall on opposite halves of the bank line. Without
+// the second term every transposed read took two extra cycles (measured:
+// SQ_LDS_BANK_CONFLICT, two per read).
+__device__ __forceinline__ int swz_mn(int k) { return (2 * (k & 3)) ^ (8 * ((k >> 3) & 1)); }
 
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
