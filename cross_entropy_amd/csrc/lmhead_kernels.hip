@@ -358,20 +358,35 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
     uint32_t sta, stb, step;   // LDS targets of load 0 and the step between loads
     bool scratch;
   };
-  auto plan = [&](int k) {
-    const int g2 = k + 2;
-    const bool own = g2 < nk;
-    const bool next = !own && chain && (g2 - nk) < nk;
-    const int k0 = own ? g2 * kBK : (next ? (g2 - nk) * kBK : 0);
-    Issue is;
-    is.ba = slice_base<A_MN>(A, next ? nA_base : A.base, k0, !next);
-    is.bb = slice_base<false>(B, next ? nB_base : B.base, k0, !next);
-    is.scratch = !(own || next);
-    const uint32_t st = base + ((p0 + k) & 1) * kStageBytes + wave_off;
-    is.sta = __builtin_amdgcn_readfirstlane(is.scratch ? scratch_row : st);
-    is.stb = __builtin_amdgcn_readfirstlane(is.scratch ? scratch_row : st + kOpBytes);
-    is.step = is.scratch ? 0u : 1024u;
-    return is;
+  // The plan of iteration k is scalar work (~20 to 40 SALU instructions).
+  // Issued in one piece it would stall the matrix pipe (one wave per SIMD
+  // issues one instruction per 4 cycles, so only 3 fit beside each 16-cycle
+  // MFMA); it is therefore computed in four pieces at four MFMA slots of the
+  // previous iteration (plan_piece(n), n = 0..3), where no loads are issued.
+  bool pl_own = false, pl_next = false;
+  int pl_k0 = 0;
+  auto plan_piece = [&](int k, int n, Issue& is) {
+    if (n == 0) {
+      const int g2 = k + 2;
+      pl_own = g2 < nk;
+      pl_next = !pl_own && chain && (g2 - nk) < nk;
+      pl_k0 = pl_own ? g2 * kBK : (pl_next ? (g2 - nk) * kBK : 0);
+    } else if (n == 1) {
+      is.ba = slice_base<A_MN>(A, pl_next ? nA_base : A.base, pl_k0, !pl_next);
+    } else if (n == 2) {
+      is.bb = slice_base<false>(B, pl_next ? nB_base : B.base, pl_k0, !pl_next);
+    } else {
+      is.scratch = !(pl_own || pl_next);
+      const uint32_t st = base + ((p0 + k) & 1) * kStageBytes + wave_off;
+      is.sta = __builtin_amdgcn_readfirstlane(is.scratch ? scratch_row : st);
+      is.stb = __builtin_amdgcn_readfirstlane(is.scratch ? scratch_row : st + kOpBytes);
+      is.step = is.scratch ? 0u : 1024u;
+    }
+  };
+  // MFMA slots (of the 32 in the first half of a step's second MFMA pass)
+  // that carry the pieces
+  auto plan_at = [&](int k, int q, Issue& is) {
+    if (q >= 4 && q <= 16 && (q & 3) == 0) plan_piece(k, q / 4 - 1, is);
   };
   auto load = [&](const Issue& is, int d) {
     if (d < 8) dma16(la.o[d], is.ba, is.sta + d * is.step);
@@ -391,15 +406,17 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
     step_reads(0, 1, q);
     __builtin_amdgcn_sched_barrier(0);
   }
+  Issue is;   // the plan of the coming iteration
 #pragma unroll
   for (int q = 0; q < NM / 2; ++q) {
     mf(1, q);
+    plan_at(0, q, is);
     __builtin_amdgcn_sched_barrier(0);
   }
   // iteration k: publish slice k + 1, finish slice k, then the head of k + 1
+  // (and the plan of iteration k + 1)
   auto iter = [&](int k, auto last_c) {
     constexpr bool last = decltype(last_c)::value;
-    const Issue is = plan(k);
     wait_vm<0>();          // slice k + 1 (this wave's part) has landed
     __syncthreads();       // ... everybody's; and every wave has issued its reads of slice k
 #pragma unroll
@@ -421,12 +438,15 @@ __device__ __forceinline__ void mma_tile(const Operand& A, const Operand& B, int
         loads_at(is, NM / 2 + q, SPAN);
         __builtin_amdgcn_sched_barrier(0);
       }
+      Issue nxt;
 #pragma unroll
       for (int q = 0; q < NM / 2; ++q) {
         mf(1, q);
         loads_at(is, NM / 2 + NM + q, SPAN);
+        plan_at(k + 1, q, nxt);
         __builtin_amdgcn_sched_barrier(0);
       }
+      is = nxt;
     }
   };
   for (int k = 0; k < nk - 1; ++k) iter(k, std::false_type{});
@@ -723,25 +743,37 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
     const bool any_dead = __any(!live);
     const int tl = tl0 + wn * 128 + j * 16 + (lane & 15);
     uint16_t* row = s.z_dz + (int64_t)tl * s.ld_dz + vw0;
+    // the three corrections apply to few columns (a target among the
+    // wave's 128 rows for some of its 16 tokens: ~1% of columns at a large
+    // vocabulary; masked tokens; the ragged last tile): they get a path of
+    // their own, so the common one is 3 VALU operations and one exp per
+    // element (as selects on every element they were 6 times that)
+    auto column = [&](auto special_c) {
+      constexpr bool special = decltype(special_c)::value;
 #pragma unroll
-    for (int i = 0; i < kNB; ++i) {
-      pin_acc(acc[i][j]);
-      float v[4];
+      for (int i = 0; i < kNB; ++i) {
+        pin_acc(acc[i][j]);
+        float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float d = fmaf(acc[i][j][r], s.sc, nlseL);
-        const float p = fast_exp2(d);
-        float x = p * fmaf(c1, d, c0);
-        if (hit_any) x = (acc_row(i, r, lane) == tr) ? x + gl : x;
-        if (any_dead) x = live ? x : 0.0f;
-        if (ragged) x = (vw0 + acc_row(i, r, lane) < Vb) ? x : 0.0f;
-        v[r] = x;
+        for (int r = 0; r < 4; ++r) {
+          const float d = fmaf(acc[i][j][r], s.sc, nlseL);
+          const float p = fast_exp2(d);
+          float x = p * fmaf(c1, d, c0);
+          if (special) {
+            x = (acc_row(i, r, lane) == tr) ? x + gl : x;
+            x = live ? x : 0.0f;
+            x = (vw0 + acc_row(i, r, lane) < Vb) ? x : 0.0f;
+          }
+          v[r] = x;
+        }
+        uint2 w;
+        w.x = pack_bf16x2(v[0], v[1]);
+        w.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(row + acc_row(i, 0, lane)) = w;
       }
-      uint2 w;
-      w.x = pack_bf16x2(v[0], v[1]);
-      w.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(row + acc_row(i, 0, lane)) = w;
-    }
+    };
+    if (hit_any || any_dead || ragged) column(std::true_type{});
+    else column(std::false_type{});
     __builtin_amdgcn_sched_barrier(0);
   }
 }
