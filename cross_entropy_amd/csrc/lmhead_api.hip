@@ -109,7 +109,8 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, int64_t chunk_size) {
   best.off_dz1 = one;
   best.off_ht = 2 * one;
   best.off_tail = best.off_ht + (size_t)round_up(best.H_pad * best.ld_ht * 2, 256);
-  best.bytes = best.off_tail + (size_t)round_up(64 * H * 2, 256);
+  best.off_ctr = best.off_tail + (size_t)round_up(64 * H * 2, 256);
+  best.bytes = best.off_ctr + (size_t)round_up((best.n_tb * best.n_vb + 1) * 8 * 4, 256);
   return best;
 }
 
@@ -334,8 +335,14 @@ int bwd_impl(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, 
   uint16_t* dzbuf[2] = {reinterpret_cast<uint16_t*>(ws), reinterpret_cast<uint16_t*>(ws + p.off_dz1)};
   uint16_t* ht = reinterpret_cast<uint16_t*>(ws + p.off_ht);
   uint16_t* W_tail = reinterpret_cast<uint16_t*>(ws + p.off_tail);
+  int* ctr = reinterpret_cast<int*>(ws + p.off_ctr);
   const int64_t v_tail = V / 64 * 64;
-  hipError_t te = lmh::launch_transpose(hidden, H, N, H, p.N_pad, p.H_pad, targets, Vtot, ht, p.ld_ht, s);
+  const int64_t nb = p.n_tb * p.n_vb;
+  // the cotangent-tile counters start at zero (a fill kernel, not a memset:
+  // the call may be captured into a graph)
+  hipError_t te = lmh::launch_fill_zero(reinterpret_cast<float*>(ctr), (nb + 1) * 8, s);
+  if (te == hipSuccess)
+    te = lmh::launch_transpose(hidden, H, N, H, p.N_pad, p.H_pad, targets, Vtot, ht, p.ld_ht, s);
   if (te == hipSuccess && v_tail < V) te = lmh::launch_pad_rows(W + v_tail * H, V - v_tail, H, 64, W_tail, s);
   if (te != hipSuccess) return fail(LMH_ERR_HIP, "bwd: launch failed: %s", hipGetErrorString(te));
 
@@ -364,8 +371,8 @@ int bwd_impl(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, 
   st.n_ht = (int)lmh::ceil_div(H, lmh::kTileRows);
   // blocks in a fixed order (token blocks outer, vocabulary blocks inner);
   // launch j forms block j's cotangent and runs block j-1's GEMMs
-  const int64_t nb = p.n_tb * p.n_vb;
   for (int64_t j = 0; j <= nb; ++j) {
+    st.z_ctr = ctr + j * 8;
     if (j >= 1) {
       const int64_t g = j - 1;
       const int64_t tb = g / p.n_vb, vb = g % p.n_vb;

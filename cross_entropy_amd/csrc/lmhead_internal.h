@@ -38,6 +38,7 @@ struct BwdPlan {
   int64_t N_pad = 0, V_pad = 0, H_pad = 0;
   int64_t ld_dz = 0, ld_ht = 0;                   // row strides (spread_ld)
   size_t off_dz1 = 0, off_ht = 0, off_tail = 0;   // byte offsets in the workspace
+  size_t off_ctr = 0;          // 8 int32 cotangent-tile counters per launch (n_tb * n_vb + 1 launches)
   size_t bytes = 0;            // total
 };
 
@@ -89,6 +90,7 @@ struct BwdStep {
   int n_dw, n_dh, n_ht;
   // cotangent part
   uint16_t* z_dz;
+  int* z_ctr;   // this launch's 8 per-XCD tile counters (zero before the launch)
   int z_t0, z_Ct, z_v0, z_Vb, z_ntt, z_nvt;
 };
 

@@ -936,14 +936,26 @@ __device__ __forceinline__ void dh_tile(const BwdStep& s, int vid, char* lds) {
 }
 
 // One backward launch: each XCD (workgroups are dealt to the 8 XCDs
-// round-robin) takes an equal share of each kind of tile: its eighth of the
-// dW tiles and of the dh tiles (the kind with the longer K first), then its
-// eighth of the cotangent tiles, so the long tiles start first everywhere and
-// the short ones fill the tail. (Cutting the concatenated gradient-tile list
-// into eight ranges instead piles all dh tiles onto the last XCDs, which
-// doubles their share of the work when the two kinds' K differ.)
+// round-robin) takes an equal share of the gradient tiles: its eighth of the
+// dW tiles and of the dh tiles (the kind with the longer K first), so the
+// long tiles start first everywhere. (Cutting the concatenated gradient-tile
+// list into eight ranges instead piles all dh tiles onto the last XCDs, which
+// doubles their share of the work when the two kinds' K differ.) The
+// cotangent tiles follow and fill the tail. Each cotangent workgroup takes
+// one tile off an atomic counter: from its XCD's own eighth first
+// (neighbouring tiles share operand panels in its L2), and once that is used
+// up from the other XCDs' eighths, so an XCD that runs ahead takes work from
+// one that lags instead of idling (the XCDs' speeds differ by a few percent).
+// Each XCD gets kStealSlots workgroups beyond its own eighth for that; a
+// workgroup that finds every counter used up exits. Which workgroup computes
+// a tile does not change its result.
+constexpr int kStealSlots = 32;   // one round of the XCD's 32 CUs
+
+__device__ __forceinline__ int z_share_lo(int x, int n_z) { return x * n_z / 8; }
+
 __global__ __launch_bounds__(kThreads) void bwd_step_kernel(const BwdStep s) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  __shared__ int z_tile;
   const int xcd = blockIdx.x & 7;
   const int loc = blockIdx.x >> 3;
   const int n_z = s.z_ntt * s.z_nvt;
@@ -951,8 +963,6 @@ __global__ __launch_bounds__(kThreads) void bwd_step_kernel(const BwdStep s) {
   const int dw_cnt = (xcd + 1) * s.n_dw / 8 - dw_lo;
   const int dh_lo = xcd * s.n_dh / 8;
   const int dh_cnt = (xcd + 1) * s.n_dh / 8 - dh_lo;
-  const int z_lo = xcd * n_z / 8;
-  const int z_cnt = (xcd + 1) * n_z / 8 - z_lo;
   const bool dh_first = s.g_Vb > s.g_Ct;   // dh tiles run K = Vb, dW tiles K = Ct
   const int first_cnt = dh_first ? dh_cnt : dw_cnt;
   const int g_cnt = dw_cnt + dh_cnt;
@@ -963,9 +973,24 @@ __global__ __launch_bounds__(kThreads) void bwd_step_kernel(const BwdStep s) {
     } else {
       dw_tile(s, dw_lo + (dh_first ? loc - dh_cnt : loc), lds);
     }
-  } else if (loc - g_cnt < z_cnt) {
-    dz_tile(s, z_lo + loc - g_cnt, lds);
+    return;
   }
+  if (n_z == 0) return;
+  if (threadIdx.x == 0) {
+    int t = -1;
+    for (int p = 0; p < 8 && t < 0; ++p) {
+      const int x = (xcd + p) & 7;
+      const int lo = z_share_lo(x, n_z);
+      const int cnt = z_share_lo(x + 1, n_z) - lo;
+      if (cnt == 0) continue;
+      const int i = __hip_atomic_fetch_add(s.z_ctr + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (i < cnt) t = lo + i;
+    }
+    z_tile = t;
+  }
+  __syncthreads();
+  const int tile = z_tile;
+  if (tile >= 0) dz_tile(s, tile, lds);
 }
 
 // Transposed bf16 copy: out[c][r] = in[r][c] for r < R and c < C, 0 for the
@@ -1080,7 +1105,7 @@ hipError_t launch_bwd_step(const BwdStep& st, hipStream_t stream) {
   int per = 0;
   for (int x = 0; x < 8; ++x)
     per = max(per, ((x + 1) * st.n_dw / 8 - x * st.n_dw / 8) + ((x + 1) * st.n_dh / 8 - x * st.n_dh / 8) +
-                       ((x + 1) * n_z / 8 - x * n_z / 8));
+                       ((x + 1) * n_z / 8 - x * n_z / 8) + (n_z > 0 ? kStealSlots : 0));
   if (per == 0) return hipSuccess;
   const int n_g = st.n_dw + st.n_dh;
   const double H = (double)st.H;
