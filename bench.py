@@ -123,9 +123,9 @@ def main() -> int:
 
     import cross_entropy_amd as lm
     from cross_entropy_amd import _native
-    from synthetic import CONFIGS, make_cotangents, make_inputs
+    from synthetic import WORKLOADS, make_cotangents, make_inputs
 
-    cfg = CONFIGS[args.workload]
+    cfg = WORKLOADS[args.workload]
     N, H, V, C = cfg.N, cfg.H, cfg.V, (args.chunk or cfg.chunk_size)
     lm.load()
     dev = torch.device("cuda:0")

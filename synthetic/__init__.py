@@ -30,7 +30,7 @@ import numpy as np
 
 __all__ = [
     "Workload",
-    "CONFIGS",
+    "WORKLOADS",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
     "make_inputs",
@@ -60,7 +60,7 @@ class Workload:
 
 
 # Distribution notation N(0, s): s is the standard deviation.
-CONFIGS = {
+WORKLOADS = {
     1: Workload(1, "tiny", 256, 256, 4096, (128,), "normal", 2.0 / np.sqrt(256.0)),
     2: Workload(2, "qwen3-4b-head-1seq", 4096, 2560, 151936, (512,), "normal_rms1", 0.02),
     3: Workload(3, "qwen3-4b-head-bs16x4096", 65536, 2560, 151936, (512,), "normal_rms1", 0.02),
@@ -90,8 +90,8 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _rng(cfg_index: int, stream: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(1000 * cfg_index + stream))
+def _rng(workload_no: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(1000 * workload_no + stream))
 
 
 def _normal_f32(rng: np.random.Generator, shape, std: float, block_rows: int = 4096) -> np.ndarray:

@@ -14,7 +14,7 @@ import pytest
 
 import oracle.lmhead_oracle as O
 from gpu_common import assert_grad_close, assert_stats_close, log, run_head
-from synthetic import CONFIGS, make_cotangents, make_inputs, sample_tokens
+from synthetic import WORKLOADS, make_cotangents, make_inputs, sample_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -89,41 +89,41 @@ def test_parity_full_small(N, H, V, C, n_masked):
 
 def test_parity_tiny_workload_full():
     """Workload 1 exactly as specified, full comparison."""
-    cfg = CONFIGS[1]
+    cfg = WORKLOADS[1]
     h, W, t = make_inputs(cfg)
     g_l, g_e = make_cotangents(cfg)
     _check_full(h, W, t, cfg.chunk_size, g_l, g_e, "workload 1")
 
 
-@pytest.mark.parametrize("cfg_index,chunk", [(2, 512), (3, 512), (4, 1024), (4, 4096), (5, 4096)])
-def test_parity_workload_sampled(cfg_index, chunk):
+@pytest.mark.parametrize("workload_no,chunk", [(2, 512), (3, 512), (4, 1024), (4, 4096), (5, 4096)])
+def test_parity_workload_sampled(workload_no, chunk):
     """Full-size workloads: all outputs computed on the GPU, the oracle
     evaluates 128 sampled tokens (plus masked samples) one by one; dW is
     checked on a second backward whose cotangents vanish outside the sample."""
-    cfg = CONFIGS[cfg_index]
-    log(f"[parity] workload {cfg_index} chunk {chunk}: generating inputs")
+    cfg = WORKLOADS[workload_no]
+    log(f"[parity] workload {workload_no} chunk {chunk}: generating inputs")
     h, W, t = make_inputs(cfg)
     g_l, g_e = make_cotangents(cfg)
     V = cfg.V
-    log(f"[parity] workload {cfg_index}: GPU dense run")
+    log(f"[parity] workload {workload_no}: GPU dense run")
     got = run_head(h, W, t, chunk, g_l, g_e)
     valid = (t >= 0) & (t < V)
     for k in ("logp", "entropy", "lse"):
         assert np.all(got[k][~valid] == 0.0), f"masked {k}"
         assert np.all(np.isfinite(got[k])), f"non-finite {k}"
     assert np.all(got["dh"][~valid] == 0.0), "masked dh rows"
-    idx = sample_tokens(t, 128, seed=cfg_index, include_masked=8)
-    log(f"[parity] workload {cfg_index}: oracle on {idx.size} sampled tokens")
+    idx = sample_tokens(t, 128, seed=workload_no, include_masked=8)
+    log(f"[parity] workload {workload_no}: oracle on {idx.size} sampled tokens")
     ref_lp, ref_en, ref_lse = O.forward(h, W, t, chunk, tokens=idx)
     for k, ref in (("logp", ref_lp), ("entropy", ref_en), ("lse", ref_lse)):
-        assert_stats_close(got[k][idx], ref, f"workload {cfg_index} {k}")
+        assert_stats_close(got[k][idx], ref, f"workload {workload_no} {k}")
     sl = np.zeros_like(g_l)
     se = np.zeros_like(g_e)
     sl[idx], se[idx] = g_l[idx], g_e[idx]
     ref_dh, ref_dW = O.backward(h, W, t, chunk, sl, se, tokens=idx)
-    rh = assert_grad_close(got["dh"][idx], ref_dh, f"workload {cfg_index} dh (sampled rows)")
-    log(f"[parity] workload {cfg_index}: GPU sparse-cotangent run")
+    rh = assert_grad_close(got["dh"][idx], ref_dh, f"workload {workload_no} dh (sampled rows)")
+    log(f"[parity] workload {workload_no}: GPU sparse-cotangent run")
     sparse = run_head(h, W, t, chunk, sl, se)
-    rw = assert_grad_close(sparse["dW"], ref_dW, f"workload {cfg_index} dW (sparse cotangents)")
+    rw = assert_grad_close(sparse["dW"], ref_dW, f"workload {workload_no} dW (sparse cotangents)")
     assert np.array_equal(sparse["dh"][idx], got["dh"][idx]), "dh rows depend only on their own cotangents"
-    log(f"[parity] workload {cfg_index}: dh frob {rh:.2e}, dW frob {rw:.2e}")
+    log(f"[parity] workload {workload_no}: dh frob {rh:.2e}, dW frob {rw:.2e}")

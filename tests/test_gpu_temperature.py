@@ -6,7 +6,7 @@ import pytest
 
 import oracle.lmhead_oracle as O
 from gpu_common import assert_grad_close, assert_stats_close, log, run_head
-from synthetic import CONFIGS, f32_to_bf16_bits, make_cotangents, make_inputs, sample_tokens
+from synthetic import WORKLOADS, f32_to_bf16_bits, make_cotangents, make_inputs, sample_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -64,7 +64,7 @@ def test_tempered_workload_2_sampled():
     """The one-sequence Qwen3-4B-shaped head (N 4096, H 2560, V 151936,
     chunk 512) at T = 0.7: sampled tokens against the oracle; dW on a second
     run with cotangents zeroed outside the sample."""
-    cfg = CONFIGS[2]
+    cfg = WORKLOADS[2]
     h, W, t = make_inputs(cfg)
     g_l, g_e = make_cotangents(cfg)
     T = 0.7
