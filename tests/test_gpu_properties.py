@@ -29,7 +29,9 @@ def _case(seed, N, H, V, w_std=0.05, n_masked=0):
 
 
 def test_bitwise_deterministic():
-    """Two runs give identical bits: fixed reduction orders, no atomics."""
+    """Two runs give identical bits: fixed reduction orders (the only atomics
+    pick which workgroup computes a cotangent tile, which does not change the
+    tile's values)."""
     h, W, t, g_l, g_e = _case(1, 1100, 256, 5000, n_masked=30)
     log("[props] determinism")
     a = run_head(h, W, t, 64, g_l, g_e)
@@ -150,6 +152,25 @@ def test_runs_on_a_non_default_stream_and_reuses_one_workspace():
     side.synchronize()
     for k, v in (("logp", logp), ("entropy", ent), ("lse", lse), ("dh", dh), ("dW", dW)):
         assert np.array_equal(v.cpu().numpy(), ref[k]), k
+
+
+def test_backward_twice_on_one_workspace():
+    """The backward's per-launch tile counters live in the workspace and are
+    reset by each call: a second backward on the same (now dirty) workspace
+    gives the same bits, on a shape with many cotangent tiles per launch."""
+    import torch
+    import cross_entropy_amd as lm
+    h, W, t, g_l, g_e = _case(11, 2304, 256, 9000, n_masked=25)
+    log("[props] backward twice on one workspace")
+    hd, Wd, td, gl, ge = dev_bits(h), dev_bits(W), dev(t), dev(g_l), dev(g_e)
+    ws = lm.workspace_for(hd, Wd, 1024, with_backward=True)
+    logp, ent, lse = lm.forward(hd, Wd, td, 1024, workspace=ws)
+    dh1, dW1 = lm.backward(hd, Wd, td, 1024, lse, ent, gl, ge, workspace=ws)
+    dh2, dW2 = lm.backward(hd, Wd, td, 1024, lse, ent, gl, ge, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dh1, dh2) and torch.equal(dW1, dW2)
+    ref = run_head(h, W, t, 1024, g_l, g_e)
+    assert np.array_equal(dh1.cpu().numpy(), ref["dh"]) and np.array_equal(dW1.cpu().numpy(), ref["dW"])
 
 
 def test_tracing_counts_launches():
