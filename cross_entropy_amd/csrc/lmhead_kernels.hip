@@ -746,8 +746,9 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
     // the three corrections apply to few columns (a target among the
     // wave's 128 rows for some of its 16 tokens: ~1% of columns at a large
     // vocabulary; masked tokens; the ragged last tile): they get a path of
-    // their own, so the common one is 3 VALU operations and one exp per
-    // element (as selects on every element they were 6 times that)
+    // their own, so the common one is three arithmetic operations and one
+    // exp per element (4.4 VALU instructions with the bf16 packing and the
+    // addresses; as selects on every element they took 13)
     auto column = [&](auto special_c) {
       constexpr bool special = decltype(special_c)::value;
 #pragma unroll
