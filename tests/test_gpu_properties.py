@@ -173,6 +173,51 @@ def test_backward_twice_on_one_workspace():
     assert np.array_equal(dh1.cpu().numpy(), ref["dh"]) and np.array_equal(dW1.cpu().numpy(), ref["dW"])
 
 
+def _rel_fro(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30)
+
+
+def test_token_permutation_is_exact():
+    """Each token's logits, statistics and dh row are computed in an order
+    that does not depend on where the token sits: permuting the tokens
+    permutes logp, entropy, lse and the rows of dh bit for bit. dW sums over
+    tokens, so only its float32 summation order changes."""
+    h, W, t, g_l, g_e = _case(12, 1100, 256, 3000, n_masked=15)
+    perm = np.random.default_rng(12).permutation(h.shape[0])
+    log("[props] token permutation")
+    a = run_head(h, W, t, 128, g_l, g_e)
+    b = run_head(h[perm], W, t[perm], 128, g_l[perm], g_e[perm])
+    for k in ("logp", "entropy", "lse", "dh"):
+        assert np.array_equal(b[k], a[k][perm]), k
+    assert _rel_fro(b["dW"], a["dW"]) < 1e-5
+
+
+def test_vocabulary_permutation_is_equivariant():
+    """Permuting W's rows (targets remapped) gives the same statistics up to
+    float32 summation order over the vocabulary and permutes dW's rows. The
+    cotangent is rounded to bf16, so the last-bit differences of lse can flip
+    a rare rounding: the gradients are compared at 2e-4 (relative Frobenius)."""
+    h, W, t, g_l, g_e = _case(13, 700, 256, 2500, n_masked=11)
+    V = W.shape[0]
+    pv = np.random.default_rng(13).permutation(V)
+    inv = np.empty(V, np.int64)
+    inv[pv] = np.arange(V)
+    t2 = np.where((t >= 0) & (t < V), inv[np.clip(t, 0, V - 1)], t).astype(np.int32)
+    log("[props] vocabulary permutation")
+    a = run_head(h, W, t, 256, g_l, g_e)
+    b = run_head(h, W[pv], t2, 256, g_l, g_e)
+    for k in ("logp", "entropy", "lse"):
+        err = np.abs(b[k].astype(np.float64) - a[k])
+        assert np.all(err <= 1e-5 + 1e-5 * np.abs(a[k])), (k, err.max())
+    assert _rel_fro(b["dh"], a["dh"]) < 2e-4
+    assert _rel_fro(b["dW"], a["dW"][pv]) < 2e-4
+    masked = ~((t >= 0) & (t < V))
+    for k in ("logp", "entropy", "lse", "dh"):
+        assert not np.any(b[k][masked]), k
+
+
 def test_tracing_counts_launches():
     import cross_entropy_amd as lm
     from cross_entropy_amd import _native
