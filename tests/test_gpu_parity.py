@@ -81,6 +81,7 @@ def test_golden_bruteforce_case():
     (513, 256, 4097, 4096, 5),     # one chunk larger than N; vocabulary one past a tile
     (64, 64, 5, 1, 3),             # fewer vocabulary rows than one MFMA block
     (2048, 256, 20000, 512, 9),    # 27 forward splits of 3 chained vocabulary tiles; the last tile ragged
+    (1, 128, 777, 1, 0),           # one token: one cotangent tile per launch, 7 XCDs with nothing to take
 ])
 def test_parity_full_small(N, H, V, C, n_masked):
     h, W, t, g_l, g_e = _case(N * 7 + V, N, H, V, n_masked=n_masked, masked_ids=(-1, V, -3))
