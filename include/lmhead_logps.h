@@ -42,8 +42,9 @@
  *    (it is kept as two bf16 buffers of a block of tokens x vocabulary, the
  *    next block's formed while the current one's is used). The backward
  *    workspace also holds a bf16 transpose of the hidden states
- *    (input-sized) and a copy of W's last V % 64 rows. The forward
- *    holds no [tokens, vocab] transient at all. Per-token forward results do not depend on
+ *    (input-sized), a copy of W's last V % 64 rows and 32 bytes of tile
+ *    counters per block (reset by every call). The forward holds no
+ *    [tokens, vocab] transient at all. Per-token forward results do not depend on
  *    chunk_size; gradients depend on it only through float32 summation order.
  *  - Targets outside [0, V) (-1 included) mask the token: its logp, entropy
  *    and lse are written as 0, its dh row is written as 0 and it adds nothing
