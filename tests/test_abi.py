@@ -204,6 +204,39 @@ def _operand_copies(N, H, V):
     return 2 * _pad(H) * _spread(_pad(max(N, 1))) + _pad(64 * H * 2)
 
 
+def _backward_blocks(N, H, V, C):
+    """The backward's block shape as the host chooses it: token-block edge
+    ct and vocabulary-block edge vb (multiples of 256, the two bf16 cotangent
+    buffers within one float32 [C, V] tensor) minimising the float32
+    accumulation traffic plus a per-launch cost; blocks evened out."""
+    T = 256
+    N = max(N, 1)
+    budget = max(float(C) * V, float(T * _spread(T)))
+    best, best_t = None, 1e300
+    for ct in range(T, _pad(N) + 1, T):
+        vb = min((int(budget / ct) - 64) // T * T, _pad(V))
+        if vb < T:
+            break
+        n_tb, n_vb = -(-N // ct), -(-V // vb)
+        t = (n_tb * n_vb + 1) * 20e-6 + (8.0 * N * H * n_vb + 8.0 * V * H * n_tb) / 5e12
+        if t < best_t:
+            best_t, best = t, (n_tb, _pad(-(-N // n_tb)), n_vb, _pad(-(-V // n_vb)))
+    return best
+
+
+def test_headline_backward_plan():
+    """The headline shape's backward runs 8 token blocks of 8192 x 17
+    vocabulary blocks of 8960: the plan that minimises the float32
+    accumulation traffic within chunk 512's budget. The library's workspace
+    size agrees with that layout to the byte."""
+    N, H, V, C = 65536, 2560, 151936, 512
+    n_tb, ct, n_vb, vb = _backward_blocks(N, H, V, C)
+    assert (n_tb, ct, n_vb, vb) == (8, 8192, 17, 8960)
+    dz = _pad(ct * _spread(vb) * 2)
+    expect = 2 * dz + _pad(_pad(H) * _spread(_pad(N)) * 2) + _pad(64 * H * 2) + _pad((n_tb * n_vb + 1) * 8 * 4)
+    assert nat.raw_workspace_bytes(N, H, V, C, True) == max(expect, nat.raw_workspace_bytes(N, H, V, C, False))
+
+
 @pytest.mark.parametrize("N,H,V,C", SHAPES)
 def test_backward_transient_within_one_f32_chunk_of_logits(N, H, V, C):
     """The backward's [tokens, vocab]-shaped transient (the cotangent block,
