@@ -218,6 +218,39 @@ def test_vocabulary_permutation_is_equivariant():
         assert not np.any(b[k][masked]), k
 
 
+def test_hip_graph_capture_and_replay():
+    """The forward and backward enqueue kernels only (no memset, no
+    synchronisation, no allocation by the library), so both can be captured
+    into one HIP graph. Each of several replays, with eager work and a
+    synchronisation between them, gives the eager run's bits."""
+    import torch
+    import cross_entropy_amd as lm
+    h, W, t, g_l, g_e = _case(14, 1300, 256, 4100, n_masked=9)
+    log("[props] graph capture")
+    hd, Wd, td, gl, ge = dev_bits(h), dev_bits(W), dev(t), dev(g_l), dev(g_e)
+    ws = lm.workspace_for(hd, Wd, 512, with_backward=True)
+    ref = run_head(h, W, t, 512, g_l, g_e)
+    dh = torch.empty((h.shape[0], h.shape[1]), dtype=torch.float32, device="cuda")
+    dW = torch.empty((W.shape[0], W.shape[1]), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):      # warm the binding up outside the capture
+        lm.forward(hd, Wd, td, 512, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        logp, ent, lse = lm.forward(hd, Wd, td, 512, workspace=ws)
+        lm.backward(hd, Wd, td, 512, lse, ent, gl, ge, workspace=ws, dh=dh, dW=dW)
+    for rep in range(3):
+        dh.fill_(float("nan"))
+        dW.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in (("logp", logp), ("entropy", ent), ("lse", lse), ("dh", dh), ("dW", dW)):
+            assert np.array_equal(v.cpu().numpy(), ref[k]), (rep, k)
+
+
 def test_tracing_counts_launches():
     import cross_entropy_amd as lm
     from cross_entropy_amd import _native
