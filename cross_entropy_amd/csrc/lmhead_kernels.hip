@@ -685,6 +685,13 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(
 //   p = 2^(z sc - lse log2e),  sc = log2(e) / T,
 // as bf16. Tokens past the block, masked tokens and vocabulary past the block
 // are written as 0, so the gradient GEMMs can run over the padded block.
+// Staging of one wave's 16 tokens x 128 vocabulary rows of dz in LDS: a
+// token's 256 bytes plus 16 of padding, so that neither the 8-byte column
+// writes nor the 16-byte row reads collide in a bank.
+constexpr int kZStageRow = 256 + 16;
+constexpr int kZStageBytes = 16 * kZStageRow;
+static_assert(4 * kZStageBytes <= kRingBytes, "staging fits in the slice ring");
+
 __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
   int vt, tt;
   raster(vid, s.z_nvt, s.z_ntt, 4, vt, tt);
@@ -718,6 +725,11 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
   f32x4 acc[kNB][kNB];
   Pipe pipe;
   mma_tile<false, 64>(oa, ob, H, lds, acc, pipe, oa.base, ob.base, false);
+  // the ring is free once every wave is past its last fragment read: each
+  // wave stages its bf16 columns there and stores whole row segments (in
+  // register layout a store instruction would cover 16 rows x 32 bytes)
+  __syncthreads();
+  char* stage = lds + wave * kZStageBytes;
 
   const int vw0 = vl0 + wm * 128;   // block-local vocabulary row of this wave
   const bool ragged = (vw0 + 128 > Vb);
@@ -741,8 +753,7 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
     const int tr = live ? (t - s.voff - v0 - vw0) : -1;
     const bool hit_any = __any(tr >= 0 && tr < 128);
     const bool any_dead = __any(!live);
-    const int tl = tl0 + wn * 128 + j * 16 + (lane & 15);
-    uint16_t* row = s.z_dz + (int64_t)tl * s.ld_dz + vw0;
+    const int tl = tl0 + wn * 128 + j * 16;   // first of the 16 tokens
     // the three corrections apply to few columns (a target among the
     // wave's 128 rows for some of its 16 tokens: ~1% of columns at a large
     // vocabulary; masked tokens; the ragged last tile): they get a path of
@@ -770,11 +781,18 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
         uint2 w;
         w.x = pack_bf16x2(v[0], v[1]);
         w.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(row + acc_row(i, 0, lane)) = w;
+        *reinterpret_cast<uint2*>(stage + (lane & 15) * kZStageRow + 2 * acc_row(i, 0, lane)) = w;
       }
     };
     if (hit_any || any_dead || ragged) column(std::true_type{});
     else column(std::false_type{});
+    // 4 tokens' 256-byte rows per store, 16 bytes a lane
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = 4 * q + (lane >> 4);
+      const uint4 x = *reinterpret_cast<const uint4*>(stage + t * kZStageRow + 16 * (lane & 15));
+      *reinterpret_cast<uint4*>(s.z_dz + (int64_t)(tl + t) * s.ld_dz + vw0 + 8 * (lane & 15)) = x;
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
