@@ -88,6 +88,31 @@ def cpu_baseline(h_bits, W_bits, targets, chunk, g_l, g_e, sample: int, N: int):
     }
 
 
+def gemm_reference(torch, h_bits, W_bits, workload: str, steps: int, warmup: int) -> int:
+    """Time the plain logits GEMM the fused forward replaces (no softmax, logits
+    materialised in bf16), through the vendor library, on the same operands.
+    A reference point only: nothing of the head's path runs here."""
+    a = h_bits.view(torch.bfloat16)
+    b = W_bits.view(torch.bfloat16)
+    N, H = a.shape
+    V = b.shape[0]
+    out = torch.empty((N, V), dtype=torch.bfloat16, device=a.device)
+    for _ in range(max(warmup, 1)):
+        torch.mm(a, b.t(), out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        torch.mm(a, b.t(), out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"gemm_reference": "torch.mm bf16 h @ W.T -> bf16 [N, V] (hipBLASLt)",
+                      "workload": workload, "N": N, "H": H, "V": V, "steps": steps,
+                      "ms": round(ms, 3), "tflops": round(2.0 * N * H * V / ms / 1e9, 1)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +127,9 @@ def main() -> int:
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times), the known-size "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="only time the library's plain bf16 logits GEMM h·Wᵀ (torch.mm, hipBLASLt; "
+                         "bf16 [N, V] output) on the same inputs, for context against the fused forward")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this head runs on a single MI355X and has no "
@@ -144,6 +172,8 @@ def main() -> int:
     lse = torch.empty(N, dtype=torch.float32, device=dev)
     dh = torch.empty((N, H), dtype=torch.float32, device=dev)
     dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+    if args.gemm_reference:
+        return gemm_reference(torch, h, W, cfg.name, args.steps, args.warmup)
     ws = lm.workspace_for(h, W, C, with_backward=True)
     stream = torch.cuda.current_stream(dev)
 
