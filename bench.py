@@ -88,28 +88,59 @@ def cpu_baseline(h_bits, W_bits, targets, chunk, g_l, g_e, sample: int, N: int):
     }
 
 
-def gemm_reference(torch, h_bits, W_bits, workload: str, steps: int, warmup: int) -> int:
-    """Time the plain logits GEMM the fused forward replaces (no softmax, logits
-    materialised in bf16), through the vendor library, on the same operands.
-    A reference point only: nothing of the head's path runs here."""
+def gemm_reference(torch, h_bits, W_bits, targets, g_l, g_e, workload: str, steps: int, warmup: int) -> int:
+    """Time the plain GEMMs the fused head replaces, through the vendor library
+    (torch.mm, hipBLASLt), on the same operands: the logits h·Wᵀ (bf16 [N, V]
+    out), and the backward's dh = dz·W and dW = dzᵀ·h on a bf16 cotangent dz
+    materialised in full (built here chunk by chunk with plain torch ops from
+    the same targets and cotangents, untimed). A reference point only:
+    nothing of the head's path runs here."""
     a = h_bits.view(torch.bfloat16)
     b = W_bits.view(torch.bfloat16)
     N, H = a.shape
     V = b.shape[0]
-    out = torch.empty((N, V), dtype=torch.bfloat16, device=a.device)
-    for _ in range(max(warmup, 1)):
-        torch.mm(a, b.t(), out=out)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        torch.mm(a, b.t(), out=out)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    print(json.dumps({"gemm_reference": "torch.mm bf16 h @ W.T -> bf16 [N, V] (hipBLASLt)",
+
+    def timed(fn):
+        for _ in range(max(warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    z = torch.empty((N, V), dtype=torch.bfloat16, device=a.device)
+    ms_z = timed(lambda: torch.mm(a, b.t(), out=z))
+    # the cotangent of logp / entropy with respect to the logits, in bf16
+    dz = z
+    rows = 2048
+    for r0 in range(0, N, rows):
+        zc = torch.mm(a[r0:r0 + rows], b.t()).float()
+        logp_all = torch.log_softmax(zc, dim=1)
+        p_all = logp_all.exp()
+        ent = -(p_all * logp_all).sum(1, keepdim=True)
+        t = targets[r0:r0 + rows].long()
+        live = (t >= 0) & (t < V)
+        d = -g_e[r0:r0 + rows, None] * p_all * (logp_all + ent) - g_l[r0:r0 + rows, None] * p_all
+        d.scatter_add_(1, t.clamp(0, V - 1)[:, None], torch.where(live, g_l[r0:r0 + rows], 0.0)[:, None])
+        d[~live] = 0.0
+        dz[r0:r0 + rows] = d.to(torch.bfloat16)
+        del zc, logp_all, p_all, d
+    dzT = dz.t().contiguous()
+    dh = torch.empty((N, H), dtype=torch.bfloat16, device=a.device)
+    dW = torch.empty((V, H), dtype=torch.bfloat16, device=a.device)
+    ms_dh = timed(lambda: torch.mm(dz, b, out=dh))
+    ms_dw = timed(lambda: torch.mm(dzT, a, out=dW))
+    fl = 2.0 * N * H * V
+    print(json.dumps({"gemm_reference": "torch.mm (hipBLASLt), bf16 operands and outputs",
                       "workload": workload, "N": N, "H": H, "V": V, "steps": steps,
-                      "ms": round(ms, 3), "tflops": round(2.0 * N * H * V / ms / 1e9, 1)}), flush=True)
+                      "logits_ms": round(ms_z, 3), "logits_tflops": round(fl / ms_z / 1e9, 1),
+                      "dh_ms": round(ms_dh, 3), "dh_tflops": round(fl / ms_dh / 1e9, 1),
+                      "dW_ms": round(ms_dw, 3), "dW_tflops": round(fl / ms_dw / 1e9, 1),
+                      "three_gemms_ms": round(ms_z + ms_dh + ms_dw, 3)}), flush=True)
     return 0
 
 
@@ -128,8 +159,8 @@ def main() -> int:
                     help="only run a plain device-to-device copy of MIB MiB (5 times), the known-size "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--gemm-reference", action="store_true",
-                    help="only time the library's plain bf16 logits GEMM h·Wᵀ (torch.mm, hipBLASLt; "
-                         "bf16 [N, V] output) on the same inputs, for context against the fused forward")
+                    help="only time the library's plain bf16 GEMMs the head replaces (torch.mm, "
+                         "hipBLASLt): logits h·Wᵀ, and dz·W, dzᵀ·h on a materialised bf16 cotangent")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this head runs on a single MI355X and has no "
@@ -173,7 +204,7 @@ def main() -> int:
     dh = torch.empty((N, H), dtype=torch.float32, device=dev)
     dW = torch.empty((V, H), dtype=torch.float32, device=dev)
     if args.gemm_reference:
-        return gemm_reference(torch, h, W, cfg.name, args.steps, args.warmup)
+        return gemm_reference(torch, h, W, t, gl, ge, cfg.name, args.steps, args.warmup)
     ws = lm.workspace_for(h, W, C, with_backward=True)
     stream = torch.cuda.current_stream(dev)
 
