@@ -55,8 +55,13 @@ is finite and by 0 otherwise:
     target and NaN for a +inf target, entropy NaN;
   * a NaN entry makes lse, logp and entropy NaN;
   * a row of no finite logit (all -inf) has lse = -inf, logp = entropy = NaN.
-Gradients follow the same IEEE arithmetic (non-finite inputs generally make
-them NaN); masked rows stay exactly 0.
+Gradients follow the same IEEE arithmetic, with two readings in the
+cotangent (step 5): the entropy term is formed only for tokens with a nonzero
+entropy cotangent, and an entry of probability 0 gets no probability term.
+So with only log-prob cotangents a -inf entry's cotangent is g_l at a -inf
+target and 0 elsewhere, and the rest of the row is that of the vocabulary
+without it (the products of the two gradient matmuls stay IEEE: a cotangent
+of 0 times the -inf table entry is NaN in dh). Masked rows stay exactly 0.
 
 Readings taken where the pages leave a step open: chunk_size counts flattened
 tokens, the last chunk may be partial (tunix #2913 tests "chunks that do not
@@ -150,9 +155,23 @@ def _entropy(z: np.ndarray, lse: np.ndarray, p: np.ndarray) -> np.ndarray:
 
 
 def _cotangent(z, lse, p, ent, t, g_l, g_e) -> np.ndarray:
-    """Step 5: dz = g_l (onehot(t) - p) - g_e p (log p + entropy)."""
-    with np.errstate(invalid="ignore"):
-        dz = -g_l[:, None] * p - g_e[:, None] * p * ((z - lse[:, None]) + ent[:, None])
+    """Step 5: dz = g_l onehot(t) - p (g_l + g_e (log p + entropy)).
+
+    Two readings settle what IEEE arithmetic alone leaves open where logits
+    are non-finite (finite logits give the same values either way):
+      * the entropy term is formed only for tokens whose entropy cotangent is
+        nonzero: a token that carries only a log-prob cotangent takes the
+        one-pass form g_l (onehot - p) (tunix #2913: the backward of a loss
+        that stops the entropy's gradient), so a NaN entropy (a row with a
+        -inf entry) never reaches its gradient;
+      * an entry whose probability is exactly 0 (a -inf logit, or every
+        finite logit of a row whose lse is +inf) gets no probability term,
+        whatever the bracket holds: p (log p + H) -> 0 as p -> 0.
+    """
+    with np.errstate(invalid="ignore", over="ignore"):
+        ent_term = np.where(g_e[:, None] != 0.0, g_e[:, None] * ((z - lse[:, None]) + ent[:, None]), 0.0)
+        prob_term = np.where(p == 0.0, 0.0, p * (g_l[:, None] + ent_term))
+    dz = -prob_term
     dz[np.arange(z.shape[0]), t] += g_l
     return dz
 

@@ -438,6 +438,74 @@ def pin_nonfinite_logits():
         _close(a[fine], r[fine], 0.0, 0.0, what=f"other tokens unaffected ({name})")
 
 
+
+def pin_nonfinite_gradients():
+    """Gradients at non-finite logits. Readings: the entropy term is formed
+    only for tokens with a nonzero entropy cotangent (the one-pass g_l
+    (onehot - p) form of a loss that stops the entropy's gradient), and an
+    entry of probability 0 gets no probability term. Closed forms:
+      * -inf entry v, log-prob cotangents only: the cotangent is g_l at a -inf
+        target and 0 elsewhere in column v, so dW[v] = sum of g_l h over the
+        tokens that target v (0 when none does); every other dW row and the
+        columns of dh where W[v] is finite equal the gradients of the
+        vocabulary without v; dh's column where W[v] = -inf is 0 * -inf = NaN
+        for the other tokens and -sign(g_l) inf for the tokens targeting v;
+      * the same with entropy cotangents: the entropy is NaN, so every entry
+        of positive probability gets a NaN cotangent, while column v (p = 0)
+        keeps the closed form above;
+      * +inf entry, log-prob cotangents only: lse = +inf, every finite
+        logit's probability is 0, so dW[u] = sum of g_l h over the tokens
+        that target u for u != v, dW[v] is NaN and every unmasked dh row NaN;
+      * NaN entry: every unmasked dh row and every dW entry is NaN.
+    Masked rows stay 0 in every case."""
+    h, W, t = _special_case(seed=22, N=7, H=5, V=9)
+    N, V = h.shape[0], W.shape[0]
+    rng = np.random.default_rng(5)
+    g_l = rng.standard_normal(N) + np.where(rng.standard_normal(N) > 0, 0.5, -0.5)   # no zero
+    g_e = rng.standard_normal(N) * 0.3 + 0.05
+    v = 4
+    t[:] = np.where(t == v, 0, t)
+    t[6] = -1                          # token 6 is masked
+    hf = f64(h)
+    keep = np.array([i for i in range(V) if i != v])
+    t_red = np.where(t > v, t - 1, t)
+    live = np.array([i for i in range(N) if t[i] >= 0])
+
+    # -inf entry, no token targets it, log-prob cotangents only
+    Wm = _row_only(W, v, _BF16_NEG_INF)
+    dh, dW = O.backward(h, Wm, t, 3, g_l, None)
+    rdh, rdW = O.backward(h, W[keep], t_red, 3, g_l, None)
+    assert np.all(dW[v] == 0.0), "-inf entry: its dW row is 0 when no token targets it"
+    _close(dW[keep], rdW, 1e-13, 1e-15, what="-inf entry: other dW rows = vocabulary without it")
+    _close(dh[:, 1:], rdh[:, 1:], 1e-13, 1e-15, what="-inf entry: dh columns of finite W[v]")
+    assert np.all(np.isnan(dh[live, 0])), "-inf entry: 0 * -inf in the dh product"
+    assert np.all(dh[6] == 0.0), "masked dh row"
+    # with entropy cotangents (all nonzero): NaN entropy reaches every entry of positive probability
+    dh, dW = O.backward(h, Wm, t, 3, g_l, g_e)
+    assert np.all(dW[v] == 0.0), "-inf entry: p = 0 column carries no probability term"
+    assert np.all(np.isnan(dW[keep])), "entropy cotangent on a NaN entropy"
+    assert np.all(np.isnan(dh[live])) and np.all(dh[6] == 0.0)
+    # a token that targets the -inf entry
+    t2 = t.copy()
+    t2[1] = v
+    dh, dW = O.backward(h, Wm, t2, 3, g_l, None)
+    _close(dW[v], g_l[1] * hf[1], 1e-15, 0.0, what="-inf target: dW[v] = g_l h")
+    assert dh[1, 0] == -np.sign(g_l[1]) * np.inf, "-inf target: g_l * -inf in the dh product"
+    assert np.all(np.isfinite(dh[:, 1:])) and np.all(np.isfinite(dW)), "finite elsewhere"
+
+    # +inf entry, log-prob cotangents only
+    Wp = _row_only(W, v, _BF16_POS_INF)
+    dh, dW = O.backward(h, Wp, t, 3, g_l, None)
+    want = np.zeros((V, h.shape[1]))
+    for i in live:
+        want[t[i]] += g_l[i] * hf[i]
+    _close(dW[keep], want[keep], 1e-15, 0.0, what="+inf entry: finite entries have p = 0")
+    assert np.all(np.isnan(dW[v])) and np.all(np.isnan(dh[live])) and np.all(dh[6] == 0.0)
+
+    # NaN entry
+    dh, dW = O.backward(h, _row_only(W, v, _BF16_NAN), t, 3, g_l, g_e)
+    assert np.all(np.isnan(dW)) and np.all(np.isnan(dh[live])) and np.all(dh[6] == 0.0)
+
 ALL_PINS = [
     pin_W_zero,
     pin_h_zero,
@@ -456,4 +524,5 @@ ALL_PINS = [
     pin_temperature_fd,
     pin_temperature_limit,
     pin_nonfinite_logits,
+    pin_nonfinite_gradients,
 ]

@@ -8,7 +8,9 @@ dropped from the log-probs, max and exp-sum swapped, entropy sign flipped,
 vocabulary bound off by one, wrap of negative ids, isfinite mask dropped),
 plus transposed operands and dropped terms, and the tempered head's
 mistakes (temperature ignored or multiplied, the backward's division by the
-temperature dropped)."""
+temperature dropped), and the non-finite cotangent's readings broken (0 times
+a NaN entropy or a -inf log-probability leaking in, the entropy term formed
+without its cotangent, a probability term kept where the probability is 0)."""
 import numpy as np
 import pytest
 
@@ -106,6 +108,31 @@ def _m_entropy_zero_times_log_zero(z, lse, p):
         return -np.sum(np.where(p > 0, p * (z - lse[:, None]), 0.0), axis=1)
 
 
+
+def _m_cotangent_plain_ieee(z, lse, p, ent, t, g_l, g_e):
+    # no selects: 0 * NaN (a NaN entropy under a zero entropy cotangent) and
+    # 0 * -inf (log p at p = 0) leak into the cotangent
+    with np.errstate(invalid="ignore"):
+        dz = -g_l[:, None] * p - g_e[:, None] * p * ((z - lse[:, None]) + ent[:, None])
+    dz[np.arange(z.shape[0]), t] += g_l
+    return dz
+
+
+def _m_entropy_term_without_cotangent(z, lse, p, ent, t, g_l, g_e):
+    with np.errstate(invalid="ignore", over="ignore"):
+        bracket = g_l[:, None] + g_e[:, None] * ((z - lse[:, None]) + ent[:, None])
+        dz = -np.where(p == 0.0, 0.0, p * bracket)
+    dz[np.arange(z.shape[0]), t] += g_l
+    return dz
+
+
+def _m_prob_term_at_zero_probability(z, lse, p, ent, t, g_l, g_e):
+    with np.errstate(invalid="ignore", over="ignore"):
+        ent_term = np.where(g_e[:, None] != 0.0, g_e[:, None] * ((z - lse[:, None]) + ent[:, None]), 0.0)
+        dz = -p * (g_l[:, None] + ent_term)
+    dz[np.arange(z.shape[0]), t] += g_l
+    return dz
+
 _orig = {}
 
 MUTANTS = {
@@ -128,6 +155,9 @@ MUTANTS = {
     "backward_temperature_division_dropped": ("_raw_cotangent", _m_backward_temperature_division_dropped),
     "lse_shift_by_nonfinite_max": ("_log_sum_exp", _m_lse_shift_always_max),
     "entropy_zero_log_zero_convention": ("_entropy", _m_entropy_zero_times_log_zero),
+    "cotangent_zero_times_nonfinite": ("_cotangent", _m_cotangent_plain_ieee),
+    "entropy_term_without_its_cotangent": ("_cotangent", _m_entropy_term_without_cotangent),
+    "probability_term_at_zero_probability": ("_cotangent", _m_prob_term_at_zero_probability),
 }
 
 
