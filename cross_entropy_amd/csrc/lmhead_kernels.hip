@@ -61,6 +61,10 @@ constexpr float kNegBig = -1.0e30f;              // "minus infinity" that keeps 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// v_mul_legacy_f32: a product that is +0 when either factor is 0, whatever
+// the other holds (inf and NaN included); IEEE otherwise.
+extern "C" __device__ float lmh_fmul_legacy(float, float) __asm("llvm.amdgcn.fmul.legacy");
+
 // NaN-propagating max (v_maximum3_f32 on gfx950): a NaN logit must reach the
 // statistics, where fmaxf would drop it.
 __device__ __forceinline__ float nan_max(float a, float b) { return __builtin_elementwise_maximum(a, b); }
@@ -744,8 +748,12 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
     const float ga = live ? gl_in[j] : 0.0f;
     const float gb = live ? ge_in[j] : 0.0f;
     const float nlseL = -L * kLog2e;
-    // dz = p * (c1 * d + c0) (+ g_l / T at the target), d = log2 p
-    const float c0 = -(ga + gb * Hn) * s.invT;
+    // dz = p * (c1 * d + c0) (+ g_l / T at the target), d = log2 p. The
+    // entropy term enters only for a nonzero entropy cotangent (selected, so
+    // a NaN entropy under g_ent = 0 stays out), and an entry of probability
+    // 0 gets no probability term (the legacy product: 0 * -inf and 0 * NaN
+    // give 0 there, a -inf logit or a row whose lse is +inf)
+    const float c0 = -(ga + (gb != 0.0f ? gb * Hn : 0.0f)) * s.invT;
     const float c1 = -(gb * kLn2) * s.invT;
     const float gl = ga * s.invT;
     // target row relative to this wave's rows (a target of another shard or
@@ -770,7 +778,7 @@ __device__ __forceinline__ void dz_tile(const BwdStep& s, int vid, char* lds) {
         for (int r = 0; r < 4; ++r) {
           const float d = fmaf(acc[i][j][r], s.sc, nlseL);
           const float p = fast_exp2(d);
-          float x = p * fmaf(c1, d, c0);
+          float x = lmh_fmul_legacy(p, fmaf(c1, d, c0));
           if (special) {
             x = (acc_row(i, r, lane) == tr) ? x + gl : x;
             x = live ? x : 0.0f;
@@ -1134,9 +1142,10 @@ hipError_t launch_bwd_step(const BwdStep& st, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_step_kernel, dim3(8 * per), dim3(kThreads), 0, stream, st);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // algorithmic work: 2 Ct Vb H per GEMM (dh, dW, and the recomputed logits);
-  // bytes: the dz block written once and read once, operand panels, f32 outputs
-  const double fl = (n_g ? 4.0 * gc * gv * H : 0.0) + (n_z ? 2.0 * zc * zv * H : 0.0);
+  // algorithmic (credited) work: 2 Ct Vb H for each of the dh and dW GEMMs;
+  // the recomputed logits (2 Ct' Vb' H more) are executed but not counted.
+  // Bytes: the dz block written once and read once, operand panels, f32 outputs
+  const double fl = n_g ? 4.0 * gc * gv * H : 0.0;
   const double by = (n_g ? 2.0 * gc * gv + 2.0 * (gc + gv) * H +
                                4.0 * H * (gc * (1 + st.g_acc_dh) + gv * (1 + st.g_acc_dW)) : 0.0) +
                     (n_z ? 2.0 * zc * zv + 2.0 * (zc + zv) * H + 20.0 * zc : 0.0);

@@ -66,8 +66,17 @@
  *    lse = +inf, logp = -inf (NaN when the target is the +inf entry) and a
  *    NaN entropy; any NaN entry makes the row's three values NaN; a row of
  *    no finite logit has lse = -inf and NaN logp and entropy. Gradients
- *    follow the same arithmetic, so non-finite inputs generally make dh and
- *    dW NaN. Masked rows are 0 whatever their hidden row holds.
+ *    follow the same arithmetic with two readings in the cotangent: the
+ *    entropy term is formed only for tokens with a nonzero g_ent (the
+ *    one-pass g_logp (onehot - p) of a loss that stops the entropy's
+ *    gradient, tunix #2913), and an entry whose probability is 0 gets no
+ *    probability term. So with only log-prob cotangents a -inf entry's
+ *    cotangent is g_logp at its targets and 0 elsewhere and the rest of the
+ *    row's cotangent is that of the vocabulary without it; the two gradient
+ *    products stay IEEE (0 times the -inf table entry is NaN in dh). A +inf
+ *    or NaN entry, or a nonzero g_ent on a NaN entropy, makes the cotangent
+ *    of that row NaN where the probability is not 0. Masked rows are 0
+ *    whatever their hidden row holds.
  *  - Return value: LMH_OK (0) or a negative LMH_ERR_* code. Argument checks
  *    run on the host before anything is enqueued, so a failing call enqueues
  *    nothing. lmhead_logps_last_error() gives a thread-local message for the
@@ -260,7 +269,11 @@ const char* lmhead_logps_version(void);
  * stops recording. lmhead_logps_trace_read(kernel, ...) waits for the
  * recorded launches to finish and returns, for that kernel, the launch
  * count, the summed duration in ms and the summed algorithmic flops and
- * bytes. This state is process-wide; enabling it adds two event records per
+ * bytes. Algorithmic flops are the credited work: 2 H per (token, vocabulary)
+ * element for the forward's logits and for each of the backward's two
+ * gradient GEMMs; the backward's recompute of the logits (another 2 H per
+ * element) is executed but not counted. This state is process-wide;
+ * enabling it adds two event records per
  * launch. Errors: LMH_ERR_ARGS (unknown kernel id), LMH_ERR_NULL.
  * lmhead_logps_trace_kernel_name returns NULL for an unknown id.
  */

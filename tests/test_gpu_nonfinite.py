@@ -1,14 +1,17 @@
 """Non-finite logits in unmasked rows on the GPU against the fp64 oracle
-(google/tunix pull request #2913 checks its fused scoring on logits with inf,
--inf and NaN entries and a row of no finite logit). Reading: IEEE evaluation
-of the definitions with the log-sum-exp shifted by the row max when finite
-and by 0 otherwise; so NaN, +inf and -inf must land exactly where the oracle
-puts them and finite values must meet the usual bar."""
+(google/tunix pull request #2913 checks its fused scoring, and the cotangent
+of its one-pass backward, on logits with inf, -inf and NaN entries and a row
+of no finite logit). Reading: IEEE evaluation of the definitions with the
+log-sum-exp shifted by the row max when finite and by 0 otherwise; in the
+cotangent, the entropy term is formed only for a nonzero entropy cotangent
+and an entry of probability 0 gets no probability term. NaN, +inf and -inf
+must land exactly where the oracle puts them, in logp / entropy / lse and in
+dh / dW, and the finite values must meet the usual bar."""
 import numpy as np
 import pytest
 
 import oracle.lmhead_oracle as O
-from gpu_common import ATOL, RTOL, log, run_head
+from gpu_common import ATOL, FROB, RTOL, frob_rel, log, run_head
 from synthetic import f32_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -36,6 +39,20 @@ def _same(gpu, ref, what):
     fin = np.isfinite(ref)
     err = np.abs(gpu[fin] - ref[fin])
     assert np.all(err <= ATOL + RTOL * np.abs(ref[fin])), f"{what}: finite values out of tolerance"
+
+
+def _same_grad(gpu, ref, what):
+    """Non-finite positions identical; the finite entries within the
+    relative Frobenius bar (exactly 0 when the oracle's are all 0)."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    for name, f in (("NaN", np.isnan), ("+inf", np.isposinf), ("-inf", np.isneginf)):
+        bad = np.argwhere(f(gpu) != f(ref))
+        assert bad.size == 0, f"{what}: {name} positions differ at {len(bad)} entries, first {bad[0].tolist()}"
+    fin = np.isfinite(ref)
+    r = frob_rel(gpu[fin], ref[fin])
+    assert r <= FROB, f"{what}: finite entries' relative Frobenius error {r:.3e}"
+    return r
 
 
 def _special_row(W, v, bits):
@@ -81,3 +98,59 @@ def test_row_of_no_finite_logit():
     plain = run_head(h, Wn, t, 64, backward=False)
     for k in ("logp", "entropy", "lse"):
         assert np.array_equal(got[k][fine], plain[k][fine]), k
+
+
+@pytest.mark.parametrize("v", [777, 100], ids=["ragged-tile", "full-tile"])
+@pytest.mark.parametrize("g_ent_mode", ["none", "dense", "half-zero"])
+@pytest.mark.parametrize("kind,bits", [("-inf", NEG_INF), ("+inf", POS_INF), ("NaN", NAN)])
+def test_nonfinite_gradients(kind, bits, g_ent_mode, v):
+    """dh and dW at a non-finite vocabulary entry against the oracle: with
+    log-prob cotangents only, a -inf entry's column carries g_l at its
+    targets and 0 elsewhere and the other gradients are those of the finite
+    head (only dh's column through the -inf table entry is 0 * -inf = NaN);
+    with entropy cotangents the NaN entropy reaches the entries of positive
+    probability; half-zero entropy cotangents mix both in one wave."""
+    h, W, t = _case(seed=41 + v)
+    rng = np.random.default_rng(v)
+    N = t.size
+    valid = t >= 0
+    t[np.flatnonzero(valid)[:4]] = v          # a few tokens target the special entry
+    g_l = rng.standard_normal(N).astype(np.float32)
+    if g_ent_mode == "none":
+        g_e = None
+    else:
+        g_e = (rng.standard_normal(N) * 0.1).astype(np.float32)
+        if g_ent_mode == "half-zero":
+            g_e[::2] = 0.0
+    Ws = _special_row(W, v, bits)
+    log(f"[nonfinite] gradients: {kind} entry at {v}, g_ent {g_ent_mode}")
+    got = run_head(h, Ws, t, 64, g_l, g_e, backward=True)
+    ref_dh, ref_dW = O.backward(h, Ws, t, 64, g_l, g_e)
+    assert np.all(got["dh"][~valid] == 0.0), "masked dh rows"
+    rh = _same_grad(got["dh"], ref_dh, f"{kind} {g_ent_mode} dh")
+    rw = _same_grad(got["dW"], ref_dW, f"{kind} {g_ent_mode} dW")
+    if kind == "-inf" and g_ent_mode == "none":
+        # the closed form: finite everywhere but dh's column through W[v] = -inf
+        assert np.all(np.isfinite(got["dW"])) and np.all(np.isfinite(got["dh"][:, 1:]))
+    log(f"[nonfinite] {kind} {g_ent_mode}: finite dh frob {rh:.2e}, dW frob {rw:.2e}")
+
+
+def test_row_of_no_finite_logit_gradients():
+    """A token whose logits are all -inf: lse = -inf, its cotangent NaN, so
+    its dh row and every dW row (its hidden row holds +inf) are NaN; the
+    masked rows stay 0."""
+    h, W, t = _case(33)
+    Wn = W.copy()
+    Wn[:, 0] = f32_to_bf16_bits(-(np.abs(O.widen_bf16(W[:, 0])) + 0.125).astype(np.float32))
+    hn = h.copy()
+    rows = [7, 200]
+    t[rows] = [5, 999]
+    hn[rows] = 0
+    hn[rows, 0] = POS_INF
+    rng = np.random.default_rng(3)
+    g_l = rng.standard_normal(t.size).astype(np.float32)
+    log("[nonfinite] gradients: rows of no finite logit")
+    got = run_head(hn, Wn, t, 64, g_l, None)
+    ref_dh, ref_dW = O.backward(hn, Wn, t, 64, g_l, None)
+    _same_grad(got["dh"], ref_dh, "no finite logit dh")
+    _same_grad(got["dW"], ref_dW, "no finite logit dW")
