@@ -17,6 +17,8 @@ Entry points mirror the C ABI:
     lmhead_logps_bwd_ex  (tempered backward that can add into dh / dW)
     lmhead_logps_fwd_shard / lmhead_logps_merge_shards / lmhead_logps_bwd_shard
                          (the head over vocabulary shards, partials merged by log-sum-exp)
+    lmhead_logps_fwd_noalloc  (tempered forward without a workspace, for callers
+                         that cannot allocate; its scratch is a fixed device array)
 two allocating helpers, ``forward`` and ``backward`` (``temperature=``
 selects the tempered calls, ``dh=`` / ``dW=`` with ``accumulate=`` add into
 caller buffers), and ``lmhead_logps``, a ``torch.autograd.Function`` front
@@ -40,6 +42,7 @@ __all__ = [
     "lmhead_logps_fwd_shard",
     "lmhead_logps_merge_shards",
     "lmhead_logps_bwd_shard",
+    "lmhead_logps_fwd_noalloc",
     "lmhead_logps",
     "forward",
     "backward",
@@ -133,6 +136,20 @@ def lmhead_logps_fwd_temp(hidden, W, targets, chunk_size: int, temperature: floa
     """Enqueue the tempered forward (logits / temperature) on ``stream``."""
     ptrs, outs = _fwd_args(hidden, W, targets, chunk_size, logp, entropy, lse, workspace, stream)
     _native.check(_native.raw_fwd_temp(*ptrs, temperature, *outs))
+
+
+def lmhead_logps_fwd_noalloc(hidden, W, targets, chunk_size: int, temperature: float, logp, entropy, lse,
+                             stream=None) -> None:
+    """Enqueue the tempered forward without a workspace (the library's fixed
+    scratch array; calls that overlap on one GPU race)."""
+    torch = _torch()
+    N, H, V = _shapes(hidden, W, targets)
+    dev = hidden.device
+    _native.check(_native.raw_fwd_noalloc(
+        _ptr(hidden, "hidden", _bf16_types(), dev), _ptr(W, "W", _bf16_types(), dev),
+        _ptr(targets, "targets", (torch.int32,), dev), N, H, V, chunk_size, temperature,
+        _ptr(logp, "logp", (torch.float32,), dev, N), _ptr(entropy, "entropy", (torch.float32,), dev, N, optional=True),
+        _ptr(lse, "lse", (torch.float32,), dev, N), _stream(dev, stream)))
 
 
 def _bwd_args(hidden, W, targets, chunk_size, lse, entropy, g_logp, g_ent, dh, dW, workspace, stream):

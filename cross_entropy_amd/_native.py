@@ -32,6 +32,7 @@ EXPORTED = (
     "lmhead_logps_fwd_shard",
     "lmhead_logps_merge_shards",
     "lmhead_logps_bwd_shard",
+    "lmhead_logps_fwd_noalloc",
     "lmhead_logps_last_error",
     "lmhead_logps_version",
     "lmhead_logps_trace_enable",
@@ -100,6 +101,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lmhead_logps_bwd_shard.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, f32, p, p, p, p, p, p,
                                            ctypes.c_uint, p, sz, p]
     lib.lmhead_logps_bwd_shard.restype = ctypes.c_int
+    lib.lmhead_logps_fwd_noalloc.argtypes = [p, p, p, i64, i64, i64, i64, f32, p, p, p, p]
+    lib.lmhead_logps_fwd_noalloc.restype = ctypes.c_int
     lib.lmhead_logps_last_error.argtypes = []
     lib.lmhead_logps_last_error.restype = ctypes.c_char_p
     lib.lmhead_logps_version.argtypes = []
@@ -199,6 +202,16 @@ def raw_bwd_shard(hidden, W_shard, targets, N, H, V_shard, vocab_offset, V_total
                                          float(temperature), lse or None, entropy or None, g_logp or None,
                                          g_ent or None, dh or None, dW_shard or None, int(flags),
                                          workspace or None, int(workspace_bytes), stream or None)
+
+
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
+
+
+def raw_fwd_noalloc(hidden, W, targets, N, H, V, chunk_size, temperature, logp, entropy, lse, stream) -> int:
+    """Call lmhead_logps_fwd_noalloc with integer addresses (0 = NULL); returns the status."""
+    return load().lmhead_logps_fwd_noalloc(hidden or None, W or None, targets or None, int(N), int(H), int(V),
+                                           int(chunk_size), float(temperature), logp or None, entropy or None,
+                                           lse or None, stream or None)
 
 
 TRACE_KERNELS = ("fwd_stats_kernel", "fwd_merge_kernel", "bwd_step_kernel", "transpose_kernel",

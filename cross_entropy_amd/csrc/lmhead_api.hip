@@ -25,6 +25,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/lmhead_logps.h"
@@ -292,6 +293,67 @@ int lmhead_logps_merge_shards(const float* partials, int64_t P, const int32_t* t
                                          logp, entropy, lse, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(LMH_ERR_HIP, "merge_shards: launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // extern "C"
+
+// Scratch of the allocation-free forward (lmhead_logps_fwd_noalloc): the
+// vocabulary-split partial records, in a fixed device array that every GPU
+// the library runs on holds until the process ends. Host code never passes
+// the array's name to a kernel (on the host it only stands in for the
+// symbol): it passes the device address hipGetSymbolAddress returns, looked
+// up once per device.
+static __device__ __align__(256) char scratch[LMH_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on its first use there).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LMH_ERR_HIP, "fwd_noalloc: hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(LMH_ERR_UNSUPPORTED, "fwd_noalloc: device %d is beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(LMH_ERR_HIP, "fwd_noalloc: hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LMH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lmhead_logps_fwd_noalloc(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, int64_t N,
+                             int64_t H, int64_t V, int64_t chunk_size, float temperature, float* logp,
+                             float* entropy, float* lse, void* stream) {
+  int rc = check_shape(N, H, V, chunk_size);
+  if (rc != LMH_OK) return rc;
+  rc = check_temperature(temperature);
+  if (rc != LMH_OK) return rc;
+  if (N == 0) return ok();
+  const size_t need = lmh::plan_forward(N, H, V).bytes;
+  if (need > (size_t)LMH_NOALLOC_SCRATCH_BYTES)
+    return fail(LMH_ERR_WORKSPACE,
+                "fwd_noalloc: N = %lld needs %zu bytes of scratch, beyond the fixed %zu (use lmhead_logps_fwd_temp "
+                "with a workspace)",
+                (long long)N, need, (size_t)LMH_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != LMH_OK) return rc;
+  return fwd_impl("fwd_noalloc", hidden, W, targets, N, H, V, 0, V, chunk_size, temperature, logp, entropy, lse,
+                  nullptr, ws, (size_t)LMH_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

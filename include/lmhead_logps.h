@@ -248,6 +248,28 @@ int lmhead_logps_bwd_shard(const uint16_t* hidden, const uint16_t* W_shard, cons
                            float* dh, float* dW_shard, unsigned flags,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Forward that allocates nothing and takes no workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). The same computation and results
+ * as lmhead_logps_fwd_temp (bit for bit); its scratch (the vocabulary-split
+ * partial records) lives in a fixed device array of
+ * LMH_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
+ * the process ends. A call fits iff lmhead_logps_workspace_bytes(N, H, V,
+ * chunk_size, 0) <= LMH_NOALLOC_SCRATCH_BYTES (about 300,000 tokens at a
+ * 152k vocabulary); larger calls fail with LMH_ERR_WORKSPACE and enqueue
+ * nothing. Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (several streams or threads at once) race and must not be made;
+ * calls in stream order are safe (each call writes every record it reads).
+ * The first call on a device looks the array's address up (set-up, no
+ * allocation). Errors: as for lmhead_logps_fwd_temp, plus LMH_ERR_WORKSPACE
+ * as above and LMH_ERR_HIP if the address lookup fails.
+ */
+#define LMH_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+int lmhead_logps_fwd_noalloc(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
+                             int64_t N, int64_t H, int64_t V, int64_t chunk_size, float temperature,
+                             float* logp, float* entropy, float* lse, void* stream);
+
 /* Thread-local message of the calling thread's last failing call ("" if none). */
 const char* lmhead_logps_last_error(void);
 

@@ -269,3 +269,21 @@ def test_library_binds_to_one_hip_runtime():
     library is handed."""
     nat.load()
     assert len(nat._hip_runtimes_mapped()) == 1
+
+
+def test_noalloc_scratch_size_matches_header_and_rejects_large_calls():
+    """The fixed scratch of the allocation-free forward: its size in the
+    header equals the binding's, and a call that needs more fails with
+    LMH_ERR_WORKSPACE on the host, before any device call."""
+    src = open(HEADER).read()
+    m = re.search(r"#define LMH_NOALLOC_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", src)
+    assert m and int(m.group(1)) << 20 == nat.NOALLOC_SCRATCH_BYTES
+    a = dict(hidden=FAKE, W=FAKE, targets=FAKE, N=600_000, H=64, V=151936, chunk_size=512, temperature=1.0,
+             logp=FAKE, entropy=FAKE, lse=FAKE, stream=0)
+    assert nat.raw_workspace_bytes(600_000, 64, 151936, 512, False) > nat.NOALLOC_SCRATCH_BYTES
+    assert nat.raw_fwd_noalloc(**a) == -4
+    assert "scratch" in nat.load().lmhead_logps_last_error().decode()
+    assert nat.raw_fwd_noalloc(**dict(a, N=-1)) == -2
+    assert nat.raw_fwd_noalloc(**dict(a, H=100)) == -6
+    assert nat.raw_fwd_noalloc(**dict(a, temperature=0.0)) == -5
+    assert nat.raw_fwd_noalloc(**dict(a, N=0)) == 0

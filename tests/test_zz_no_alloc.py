@@ -1,0 +1,80 @@
+"""The allocation-free forward (lmhead_logps_fwd_noalloc) through the C ABI
+against the workspace forward (lmhead_logps_fwd_temp) it shares its kernels
+with: bit for bit, and both within the oracle's bar; two calls in a row on
+the library's fixed scratch array, the second one smaller, so a smaller call
+must not see what the larger one left there."""
+import numpy as np
+import pytest
+
+import oracle.lmhead_oracle as O
+from gpu_common import assert_stats_close, dev, dev_bits, log
+from synthetic import f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, N, H, V, n_masked):
+    rng = np.random.default_rng(seed)
+    h = f32_to_bf16_bits(rng.standard_normal((N, H)).astype(np.float32))
+    W = f32_to_bf16_bits((rng.standard_normal((V, H)) * 0.05).astype(np.float32))
+    t = rng.integers(0, V, size=N).astype(np.int32)
+    t[rng.choice(N, size=n_masked, replace=False)] = -1
+    return h, W, t
+
+
+def _both(h_bits, W_bits, t, C, T):
+    import torch
+    import cross_entropy_amd as lm
+    h, W, tt = dev_bits(h_bits), dev_bits(W_bits), dev(t)
+    N = t.size
+    out = {}
+    for kind in ("noalloc", "workspace"):
+        logp = torch.full((N,), 7.0, device="cuda")
+        ent = torch.full((N,), 7.0, device="cuda")
+        lse = torch.full((N,), 7.0, device="cuda")
+        if kind == "noalloc":
+            lm.lmhead_logps_fwd_noalloc(h, W, tt, C, T, logp, ent, lse)
+        else:
+            ws = lm.workspace_for(h, W, C, with_backward=False)
+            lm.lmhead_logps_fwd_temp(h, W, tt, C, T, logp, ent, lse, ws)
+        torch.cuda.synchronize()
+        out[kind] = {"logp": logp.cpu().numpy(), "entropy": ent.cpu().numpy(), "lse": lse.cpu().numpy()}
+    return out
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_noalloc_forward_two_calls(T):
+    import cross_entropy_amd as lm
+    calls = [(71, 9000, 256, 5003, 64, 40), (72, 700, 128, 777, 16, 9)]
+    for seed, N, H, V, C, n_masked in calls:
+        need = lm.lmhead_logps_workspace_bytes(N, H, V, C, with_backward=False)
+        log(f"[noalloc] T={T} N={N} H={H} V={V} C={C}: scratch {need} bytes")
+        h, W, t = _inputs(seed, N, H, V, n_masked)
+        got = _both(h, W, t, C, T)
+        ref = O.forward(h, W, t, C, temperature=T)
+        valid = t >= 0
+        for k, r in zip(("logp", "entropy", "lse"), ref):
+            a, b = got["noalloc"][k], got["workspace"][k]
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{k}: noalloc differs from fwd_temp"
+            assert_stats_close(a[valid], r[valid], f"noalloc {k}")
+            assert np.all(a[~valid] == 0.0), f"noalloc masked {k}"
+
+
+def test_noalloc_rejects_beyond_its_scratch():
+    """A call whose partial records exceed the fixed array fails on the host
+    with LMH_ERR_WORKSPACE and writes nothing."""
+    import torch
+    import cross_entropy_amd as lm
+    from cross_entropy_amd import _native as nat
+    N, H, V, C = 600_000, 64, 151936, 512
+    assert lm.lmhead_logps_workspace_bytes(N, H, V, C, with_backward=False) > nat.NOALLOC_SCRATCH_BYTES
+    h = torch.zeros((N, H), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((V, H), dtype=torch.bfloat16, device="cuda")
+    t = torch.zeros(N, dtype=torch.int32, device="cuda")
+    logp = torch.full((N,), 3.0, device="cuda")
+    lse = torch.full((N,), 3.0, device="cuda")
+    with pytest.raises(lm.LmheadError) as e:
+        lm.lmhead_logps_fwd_noalloc(h, W, t, C, 1.0, logp, None, lse)
+    assert e.value.code == -4
+    torch.cuda.synchronize()
+    assert bool((logp == 3.0).all()) and bool((lse == 3.0).all())
