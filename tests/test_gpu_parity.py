@@ -1,11 +1,17 @@
 """HIP path vs the fp64 oracle, through the C ABI, on seeded inputs.
 
 Small shapes are compared element by element in full (several tiles, ragged
-tails in every dimension, many backward blocks). The five workloads run at
-their full sizes in the launch configuration the benchmark times; there the
-oracle evaluates a fixed sample of tokens one by one (each token needs only
-its own logits row), and dW is checked on the same inputs with cotangents
-zeroed outside that sample, which the oracle then evaluates exactly."""
+tails in every dimension, many backward blocks). The one-sequence workload
+(N 4096, H 2560, V 151936) is compared in full: every token's statistics,
+all of dh and all of dW under the real dense cotangents. The other workloads
+run at their full sizes in the launch configuration the benchmark times;
+there the oracle evaluates a fixed sample of 1,024 tokens one by one (each
+token needs only its own logits row), and dW is checked on the same inputs
+with cotangents zeroed outside that sample, which the oracle then evaluates
+exactly. Peaked logits (logit std 8 to 16, targets planted at +30 so their
+probability rounds to 1, a row of logits near +80) cover the numerical edges
+of a trained head: the cancellation in onehot - p, the base-2 running-max
+rescale at large logits and near-zero entropy."""
 import json
 import os
 
@@ -14,7 +20,7 @@ import pytest
 
 import oracle.lmhead_oracle as O
 from gpu_common import assert_grad_close, assert_stats_close, log, run_head
-from synthetic import WORKLOADS, make_cotangents, make_inputs, sample_tokens
+from synthetic import WORKLOADS, f32_to_bf16_bits, make_cotangents, make_inputs, sample_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -96,10 +102,33 @@ def test_parity_tiny_workload_full():
     _check_full(h, W, t, cfg.chunk_size, g_l, g_e, "workload 1")
 
 
-@pytest.mark.parametrize("workload_no,chunk", [(2, 512), (3, 512), (4, 1024), (4, 4096), (5, 4096)])
+@pytest.mark.timeout(900)
+def test_parity_workload2_full():
+    """The one-sequence workload compared in full: every token's logp,
+    entropy and lse, all of dh, and all of dW under the dense cotangents."""
+    cfg = WORKLOADS[2]
+    h, W, t = make_inputs(cfg)
+    g_l, g_e = make_cotangents(cfg)
+    _check_full(h, W, t, cfg.chunk_size, g_l, g_e, "workload 2 (full)")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(3000)
+@pytest.mark.parametrize("chunk", [1024])
+def test_parity_workload4_full(chunk):
+    """The context-rank share (N 15237, H 4096) compared in full; about 10
+    minutes of host BLAS, so it runs only with --run-slow."""
+    cfg = WORKLOADS[4]
+    h, W, t = make_inputs(cfg)
+    g_l, g_e = make_cotangents(cfg)
+    _check_full(h, W, t, chunk, g_l, g_e, f"workload 4 chunk {chunk} (full)")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("workload_no,chunk", [(3, 512), (4, 1024), (4, 4096), (5, 4096)])
 def test_parity_workload_sampled(workload_no, chunk):
     """Full-size workloads: all outputs computed on the GPU, the oracle
-    evaluates 128 sampled tokens (plus masked samples) one by one; dW is
+    evaluates 1,024 sampled tokens (plus masked samples) one by one; dW is
     checked on a second backward whose cotangents vanish outside the sample."""
     cfg = WORKLOADS[workload_no]
     log(f"[parity] workload {workload_no} chunk {chunk}: generating inputs")
@@ -113,7 +142,7 @@ def test_parity_workload_sampled(workload_no, chunk):
         assert np.all(got[k][~valid] == 0.0), f"masked {k}"
         assert np.all(np.isfinite(got[k])), f"non-finite {k}"
     assert np.all(got["dh"][~valid] == 0.0), "masked dh rows"
-    idx = sample_tokens(t, 128, seed=workload_no, include_masked=8)
+    idx = sample_tokens(t, 1024, seed=workload_no, include_masked=32)
     log(f"[parity] workload {workload_no}: oracle on {idx.size} sampled tokens")
     ref_lp, ref_en, ref_lse = O.forward(h, W, t, chunk, tokens=idx)
     for k, ref in (("logp", ref_lp), ("entropy", ref_en), ("lse", ref_lse)):
@@ -128,3 +157,89 @@ def test_parity_workload_sampled(workload_no, chunk):
     rw = assert_grad_close(sparse["dW"], ref_dW, f"workload {workload_no} dW (sparse cotangents)")
     assert np.array_equal(sparse["dh"][idx], got["dh"][idx]), "dh rows depend only on their own cotangents"
     log(f"[parity] workload {workload_no}: dh frob {rh:.2e}, dW frob {rw:.2e}")
+
+
+def _peaked_case(seed, N, H, V, w_std, n_planted, n_high_row=1):
+    """Logits of std about w_std * sqrt(H) (7 to 13 here); n_planted tokens
+    whose hidden row points along their target's W row, half of them so that
+    the target logit is about +30 above the rest and its probability rounds
+    to 1 in float32, half at +8 (probabilities 0.01 to 0.5); n_high_row
+    tokens whose every logit is shifted by about +80 (a common component of
+    all W rows that only these tokens see). Masked tokens included."""
+    rng = np.random.default_rng(seed)
+    hf = rng.standard_normal((N, H)).astype(np.float32)
+    Wf = (rng.standard_normal((V, H)) * w_std).astype(np.float32)
+    Wf[:, 0] = 4.0 + rng.standard_normal(V).astype(np.float32) * np.float32(w_std)   # common component
+    hf[:, 0] = 0.0
+    t = rng.integers(0, V, size=N).astype(np.int32)
+    planted = rng.choice(N, size=n_planted, replace=False)
+    for k, i in enumerate(planted):
+        w = Wf[t[i]].copy()
+        w[0] = 0.0
+        margin = 30.0 if k % 2 == 0 else 8.0
+        hf[i] = (0.15 * hf[i] + margin * w / float(np.dot(w, w))).astype(np.float32)
+        hf[i, 0] = 0.0
+    rest = np.setdiff1d(np.arange(N), planted)
+    high = rng.choice(rest, size=n_high_row, replace=False)
+    hf[high, 0] = 20.0                     # + ~80 on every logit of these tokens
+    masked = rng.choice(np.setdiff1d(rest, high), size=max(1, N // 64), replace=False)
+    t[masked] = -1
+    h = f32_to_bf16_bits(hf)
+    W = f32_to_bf16_bits(Wf)
+    g_l = rng.standard_normal(N).astype(np.float32)
+    g_e = (rng.standard_normal(N) * 0.1).astype(np.float32)
+    return h, W, t, g_l, g_e, planted, high
+
+
+@pytest.mark.parametrize("w_std,T", [(0.5, 1.0), (1.0, 1.0), (0.5, 0.25)])
+def test_parity_peaked_logits_full(w_std, T):
+    """Peaked logits compared in full: target probabilities that round to 1
+    (onehot - p cancels), logits of std 8 to 16 (64 at T = 0.25) feeding the
+    running-max rescale, a row of logits near +80, near-zero entropies."""
+    N, H, V, C = 640, 256, 4096, 128
+    h, W, t, g_l, g_e, planted, high = _peaked_case(int(w_std * 100) + int(100 * T), N, H, V, w_std, 128)
+    log(f"[parity] peaked logits w_std={w_std} T={T}")
+    got = run_head(h, W, t, C, g_l, g_e, temperature=T)
+    ref = O.forward_backward(h, W, t, C, g_l, g_e, temperature=T)
+    valid = t >= 0
+    for k in ("logp", "entropy", "lse"):
+        assert_stats_close(got[k][valid], ref[k][valid], f"peaked {k}")
+        assert np.all(got[k][~valid] == 0.0), f"peaked masked {k}"
+    # the planted targets dominate: probability near 1, entropy near 0
+    p_t = np.exp(ref["logp"][planted[::2]])
+    assert np.all(p_t > 0.9999), "planted targets are saturated"
+    assert np.all(ref["lse"][high] > 60.0), "the high row's lse"
+    assert np.all(got["dh"][~valid] == 0.0)
+    rh = assert_grad_close(got["dh"], ref["dh"], "peaked dh")
+    rw = assert_grad_close(got["dW"], ref["dW"], "peaked dW")
+    log(f"[parity] peaked w_std={w_std} T={T}: dh frob {rh:.2e}, dW frob {rw:.2e}")
+
+
+@pytest.mark.timeout(600)
+def test_parity_peaked_logits_workload2_shape():
+    """Peaked logits at the one-sequence shape (N 4096, H 2560, V 151936,
+    chunk 512): logit std about 10, a quarter of the tokens planted, the
+    oracle on 512 sampled tokens (planted, high-row and masked ones among
+    them) with dW from cotangents vanishing outside the sample."""
+    cfg = WORKLOADS[2]
+    N, H, V, C = cfg.N, cfg.H, cfg.V, cfg.chunk_size
+    log("[parity] peaked logits at the one-sequence shape: generating")
+    h, W, t, g_l, g_e, planted, high = _peaked_case(2002, N, H, V, 0.2, N // 4, n_high_row=4)
+    got = run_head(h, W, t, C, g_l, g_e)
+    valid = t >= 0
+    for k in ("logp", "entropy", "lse"):
+        assert np.all(got[k][~valid] == 0.0) and np.all(np.isfinite(got[k])), k
+    rng = np.random.default_rng(9)
+    idx = np.unique(np.concatenate([rng.choice(np.flatnonzero(valid), 448, replace=False), planted[:32], high,
+                                    np.flatnonzero(~valid)[:28]]))
+    log(f"[parity] peaked one-sequence shape: oracle on {idx.size} tokens")
+    ref_lp, ref_en, ref_lse = O.forward(h, W, t, C, tokens=idx)
+    for k, ref in (("logp", ref_lp), ("entropy", ref_en), ("lse", ref_lse)):
+        assert_stats_close(got[k][idx], ref, f"peaked one-sequence {k}")
+    sl = np.zeros_like(g_l)
+    se = np.zeros_like(g_e)
+    sl[idx], se[idx] = g_l[idx], g_e[idx]
+    ref_dh, ref_dW = O.backward(h, W, t, C, sl, se, tokens=idx)
+    assert_grad_close(got["dh"][idx], ref_dh, "peaked one-sequence dh (sampled rows)")
+    sparse = run_head(h, W, t, C, sl, se)
+    assert_grad_close(sparse["dW"], ref_dW, "peaked one-sequence dW (sparse cotangents)")
