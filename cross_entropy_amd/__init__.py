@@ -15,6 +15,8 @@ Entry points mirror the C ABI:
     lmhead_logps_fwd_temp / lmhead_logps_bwd_temp   (the same with a temperature
                      after chunk_size: the head scores the logits divided by it)
     lmhead_logps_bwd_ex  (tempered backward that can add into dh / dW)
+    lmhead_logps_bwd_bf16  (the same writing bf16 dh / dW: float32 sums in the
+                         workspace, each element rounded once)
     lmhead_logps_fwd_shard / lmhead_logps_merge_shards / lmhead_logps_bwd_shard
                          (the head over vocabulary shards, partials merged by log-sum-exp)
     lmhead_logps_fwd_noalloc  (tempered forward without a workspace, for callers
@@ -39,6 +41,7 @@ __all__ = [
     "lmhead_logps_fwd_temp",
     "lmhead_logps_bwd_temp",
     "lmhead_logps_bwd_ex",
+    "lmhead_logps_bwd_bf16",
     "lmhead_logps_fwd_shard",
     "lmhead_logps_merge_shards",
     "lmhead_logps_bwd_shard",
@@ -90,8 +93,18 @@ def _stream(device, stream):
     return stream.cuda_stream
 
 
-def lmhead_logps_workspace_bytes(N: int, H: int, V: int, chunk_size: int, with_backward: bool = True) -> int:
-    return _native.raw_workspace_bytes(N, H, V, chunk_size, with_backward)
+def lmhead_logps_workspace_bytes(N: int, H: int, V: int, chunk_size: int, with_backward=True) -> int:
+    """Workspace bytes: with_backward False (forward only), True (forward and
+    the float32-gradient backward) or "bf16" (also the bf16-gradient backward)."""
+    return _native.raw_workspace_bytes(N, H, V, chunk_size, _ws_kind(with_backward))
+
+
+def _ws_kind(with_backward) -> int:
+    if with_backward == "bf16":
+        return _native.WS_BWD_BF16
+    if isinstance(with_backward, str):
+        raise ValueError(f"with_backward must be a bool or 'bf16', got {with_backward!r}")
+    return _native.WS_BWD if with_backward else _native.WS_FWD
 
 
 def _shapes(hidden, W, targets):
@@ -152,8 +165,11 @@ def lmhead_logps_fwd_noalloc(hidden, W, targets, chunk_size: int, temperature: f
         _ptr(lse, "lse", (torch.float32,), dev, N), _stream(dev, stream)))
 
 
-def _bwd_args(hidden, W, targets, chunk_size, lse, entropy, g_logp, g_ent, dh, dW, workspace, stream):
+def _bwd_args(hidden, W, targets, chunk_size, lse, entropy, g_logp, g_ent, dh, dW, workspace, stream,
+              grad_types=None):
     torch = _torch()
+    if grad_types is None:
+        grad_types = (torch.float32,)
     N, H, V = _shapes(hidden, W, targets)
     dev = hidden.device
     if tuple(dh.shape) != (N, H) or tuple(dW.shape) != (V, H):
@@ -169,8 +185,8 @@ def _bwd_args(hidden, W, targets, chunk_size, lse, entropy, g_logp, g_ent, dh, d
         _ptr(entropy, "entropy", (torch.float32,), dev, N, optional=True),
         _ptr(g_logp, "g_logp", (torch.float32,), dev, N, optional=True),
         _ptr(g_ent, "g_ent", (torch.float32,), dev, N, optional=True),
-        _ptr(dh, "dh", (torch.float32,), dev),
-        _ptr(dW, "dW", (torch.float32,), dev),
+        _ptr(dh, "dh", grad_types, dev),
+        _ptr(dW, "dW", grad_types, dev),
         _ptr(workspace, "workspace", (torch.uint8,), dev),
         workspace.numel(),
         _stream(dev, stream),
@@ -199,6 +215,16 @@ def lmhead_logps_bwd_ex(hidden, W, targets, chunk_size: int, temperature: float,
     ``BWD_ACCUMULATE_DW``: add into dh / dW instead of overwriting)."""
     ptrs, rest = _bwd_args(hidden, W, targets, chunk_size, lse, entropy, g_logp, g_ent, dh, dW, workspace, stream)
     _native.check(_native.raw_bwd_ex(*ptrs, temperature, *rest[:6], flags, *rest[6:]))
+
+
+def lmhead_logps_bwd_bf16(hidden, W, targets, chunk_size: int, temperature: float, lse, entropy, g_logp, g_ent,
+                          dh, dW, flags: int, workspace, stream=None) -> None:
+    """Enqueue the backward writing bf16 gradients dh [N, H] / dW [V, H]
+    (bfloat16 tensors); ``flags`` as for ``lmhead_logps_bwd_ex``; the
+    workspace is sized with ``with_backward="bf16"``."""
+    ptrs, rest = _bwd_args(hidden, W, targets, chunk_size, lse, entropy, g_logp, g_ent, dh, dW, workspace, stream,
+                           grad_types=_bf16_types())
+    _native.check(_native.raw_bwd_bf16(*ptrs, temperature, *rest[:6], flags, *rest[6:]))
 
 
 def lmhead_logps_fwd_shard(hidden, W_shard, targets, vocab_offset: int, V_total: int, chunk_size: int,
@@ -240,7 +266,9 @@ def lmhead_logps_bwd_shard(hidden, W_shard, targets, vocab_offset: int, V_total:
                                         flags, *rest[6:]))
 
 
-def workspace_for(hidden, W, chunk_size: int, with_backward: bool = True):
+def workspace_for(hidden, W, chunk_size: int, with_backward=True):
+    """Allocate a workspace (uint8 tensor) for the given calls: with_backward
+    False, True or "bf16" as for ``lmhead_logps_workspace_bytes``."""
     torch = _torch()
     N, H = hidden.shape
     V = W.shape[0]
@@ -269,21 +297,32 @@ def forward(hidden, W, targets, chunk_size: int, with_entropy: bool = True, work
 
 def backward(hidden, W, targets, chunk_size: int, lse, entropy, g_logp, g_ent: Optional = None,
              workspace=None, stream=None, temperature: Optional[float] = None, dh=None, dW=None,
-             accumulate: bool = False) -> Tuple:
-    """Run the backward: (dh, dW), float32. Gradients are allocated unless
-    ``dh`` / ``dW`` are given; with ``accumulate`` the given buffers are
-    added into. ``temperature`` must match the forward that produced lse and
-    entropy."""
+             accumulate: bool = False, grad_dtype=None) -> Tuple:
+    """Run the backward: (dh, dW), float32 (or bfloat16 with
+    ``grad_dtype=torch.bfloat16``). Gradients are allocated unless ``dh`` /
+    ``dW`` are given; with ``accumulate`` the given buffers are added into.
+    ``temperature`` must match the forward that produced lse and entropy."""
     torch = _torch()
     N, H = hidden.shape
     V = W.shape[0]
     dev = hidden.device
+    if grad_dtype is None:
+        grad_dtype = dh.dtype if dh is not None else torch.float32
+    if grad_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"grad_dtype must be float32 or bfloat16, got {grad_dtype}")
     if accumulate and (dh is None or dW is None):
         raise ValueError("accumulate needs both dh and dW buffers")
     if dh is None:
-        dh = torch.empty((N, H), dtype=torch.float32, device=dev)
+        dh = torch.empty((N, H), dtype=grad_dtype, device=dev)
     if dW is None:
-        dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+        dW = torch.empty((V, H), dtype=grad_dtype, device=dev)
+    if grad_dtype == torch.bfloat16:
+        if workspace is None:
+            workspace = workspace_for(hidden, W, chunk_size, with_backward="bf16")
+        flags = (_native.BWD_ACCUMULATE_DH | _native.BWD_ACCUMULATE_DW) if accumulate else 0
+        lmhead_logps_bwd_bf16(hidden, W, targets, chunk_size, 1.0 if temperature is None else temperature, lse,
+                              entropy, g_logp, g_ent, dh, dW, flags, workspace, stream)
+        return dh, dW
     if workspace is None:
         workspace = workspace_for(hidden, W, chunk_size, with_backward=True)
     if accumulate:
@@ -303,17 +342,20 @@ def _autograd_function():
 
     class _LmheadLogps(torch.autograd.Function):
         """logp (and entropy) of the head with its backward through the
-        library; gradients come back in the inputs' dtypes."""
+        library. The forward holds only its own small workspace (the split
+        records) and keeps lse (and entropy) for the backward; the backward
+        sizes its workspace when it runs and writes the gradients in the
+        inputs' dtype directly (bf16 inputs: lmhead_logps_bwd_bf16, float32
+        sums in the workspace, no float32 [N, H] / [V, H] gradient tensors
+        and no cast)."""
 
         @staticmethod
         def forward(ctx, hidden, W, targets, chunk_size, temperature, with_entropy):
-            ws = workspace_for(hidden, W, chunk_size, with_backward=True)
-            logp, ent, lse = forward(hidden, W, targets, chunk_size, with_entropy=with_entropy, workspace=ws,
+            logp, ent, lse = forward(hidden, W, targets, chunk_size, with_entropy=with_entropy,
                                      temperature=temperature)
             ctx.chunk_size = chunk_size
             ctx.temperature = temperature
             ctx.with_entropy = with_entropy
-            ctx.workspace = ws
             saved = (hidden, W, targets, lse) + ((ent,) if with_entropy else ())
             ctx.save_for_backward(*saved)
             if with_entropy:
@@ -326,9 +368,10 @@ def _autograd_function():
             ent = ctx.saved_tensors[4] if ctx.with_entropy else None
             gl = None if g_logp is None else g_logp.detach().contiguous().float()
             ge = None if (g_ent is None or ent is None) else g_ent.detach().contiguous().float()
+            bf16 = hidden.dtype == torch.bfloat16 and W.dtype == torch.bfloat16
             dh, dW = backward(hidden, W, targets, ctx.chunk_size, lse, ent if ge is not None else None, gl, ge,
-                              workspace=ctx.workspace, temperature=ctx.temperature)
-            ctx.workspace = None
+                              temperature=ctx.temperature,
+                              grad_dtype=torch.bfloat16 if bf16 else torch.float32)
             return (dh.to(hidden.dtype) if ctx.needs_input_grad[0] else None,
                     dW.to(W.dtype) if ctx.needs_input_grad[1] else None,
                     None, None, None, None)

@@ -9,7 +9,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liblmhead_logps.so")
+# LMHEAD_LOGPS_LIB names another build of the library to load (the host
+# sanitizer build of cross_entropy_amd/build.py --sanitize)
+LIB_PATH = os.environ.get("LMHEAD_LOGPS_LIB") or os.path.join(_PKG, "liblmhead_logps.so")
 
 LMH_OK = 0
 ERROR_NAMES = {
@@ -29,6 +31,7 @@ EXPORTED = (
     "lmhead_logps_fwd_temp",
     "lmhead_logps_bwd_temp",
     "lmhead_logps_bwd_ex",
+    "lmhead_logps_bwd_bf16",
     "lmhead_logps_fwd_shard",
     "lmhead_logps_merge_shards",
     "lmhead_logps_bwd_shard",
@@ -94,6 +97,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lmhead_logps_bwd_temp.restype = ctypes.c_int
     lib.lmhead_logps_bwd_ex.argtypes = [p, p, p, i64, i64, i64, i64, f32, p, p, p, p, p, p, ctypes.c_uint, p, sz, p]
     lib.lmhead_logps_bwd_ex.restype = ctypes.c_int
+    lib.lmhead_logps_bwd_bf16.argtypes = [p, p, p, i64, i64, i64, i64, f32, p, p, p, p, p, p, ctypes.c_uint, p, sz,
+                                          p]
+    lib.lmhead_logps_bwd_bf16.restype = ctypes.c_int
     lib.lmhead_logps_fwd_shard.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, f32, p, p, sz, p]
     lib.lmhead_logps_fwd_shard.restype = ctypes.c_int
     lib.lmhead_logps_merge_shards.argtypes = [p, i64, p, i64, i64, f32, p, p, p, p]
@@ -124,10 +130,14 @@ def check(code: int) -> None:
         raise LmheadError(code, msg)
 
 
-def raw_workspace_bytes(N: int, H: int, V: int, chunk_size: int, with_backward: bool) -> int:
+WS_FWD, WS_BWD, WS_BWD_BF16 = 0, 1, 2
+
+
+def raw_workspace_bytes(N: int, H: int, V: int, chunk_size: int, with_backward) -> int:
+    """with_backward: False / True (WS_FWD / WS_BWD) or WS_BWD_BF16."""
     out = ctypes.c_size_t(0)
-    check(load().lmhead_logps_workspace_bytes(int(N), int(H), int(V), int(chunk_size),
-                                              1 if with_backward else 0, ctypes.byref(out)))
+    check(load().lmhead_logps_workspace_bytes(int(N), int(H), int(V), int(chunk_size), int(with_backward),
+                                              ctypes.byref(out)))
     return int(out.value)
 
 
@@ -178,6 +188,15 @@ def raw_bwd_ex(hidden, W, targets, N, H, V, chunk_size, temperature, lse, entrop
                                       workspace or None, int(workspace_bytes), stream or None)
 
 
+def raw_bwd_bf16(hidden, W, targets, N, H, V, chunk_size, temperature, lse, entropy, g_logp, g_ent, dh, dW, flags,
+                 workspace, workspace_bytes, stream) -> int:
+    """Call lmhead_logps_bwd_bf16 with integer addresses (0 = NULL); returns the status."""
+    return load().lmhead_logps_bwd_bf16(hidden or None, W or None, targets or None, int(N), int(H), int(V),
+                                        int(chunk_size), float(temperature), lse or None, entropy or None,
+                                        g_logp or None, g_ent or None, dh or None, dW or None, int(flags),
+                                        workspace or None, int(workspace_bytes), stream or None)
+
+
 def raw_fwd_shard(hidden, W_shard, targets, N, H, V_shard, vocab_offset, V_total, chunk_size, temperature,
                   partial, workspace, workspace_bytes, stream) -> int:
     """Call lmhead_logps_fwd_shard with integer addresses (0 = NULL); returns the status."""
@@ -215,7 +234,7 @@ def raw_fwd_noalloc(hidden, W, targets, N, H, V, chunk_size, temperature, logp, 
 
 
 TRACE_KERNELS = ("fwd_stats_kernel", "fwd_merge_kernel", "bwd_step_kernel", "transpose_kernel",
-                 "fill_zero_kernel", "pad_rows_kernel")
+                 "fill_zero_kernel", "pad_rows_kernel", "bwd_step_bf16_kernel")
 
 
 def trace_enable(on: bool) -> None:

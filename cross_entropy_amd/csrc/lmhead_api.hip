@@ -114,6 +114,16 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, int64_t chunk_size) {
   best.off_tail = best.off_ht + (size_t)round_up(best.H_pad * best.ld_ht * 2, 256);
   best.off_ctr = best.off_tail + (size_t)round_up(64 * H * 2, 256);
   best.bytes = best.off_ctr + (size_t)round_up((best.n_tb * best.n_vb + 1) * 8 * 4, 256);
+  // the bf16-gradient backward keeps the larger gradient per block and the
+  // smaller one whole in float32
+  best.vocab_outer = N <= V;
+  const int64_t whole = best.vocab_outer ? best.N_pad : best.V_pad;
+  const int64_t part = best.vocab_outer ? best.Vb : best.Ct;
+  const size_t acc_whole = (size_t)round_up(whole * H * 4, 256);
+  const size_t acc_part = (size_t)round_up(part * H * 4, 256);
+  best.off_acc_dh = best.bytes;
+  best.off_acc_dW = best.bytes + (best.vocab_outer ? acc_whole : acc_part);
+  best.bytes_bf16 = best.bytes + acc_whole + acc_part;
   return best;
 }
 
@@ -197,8 +207,13 @@ int lmhead_logps_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t chunk_
     const int rb = check_backward_size(N, V);
     if (rb != LMH_OK) return rb;
   }
+  if (with_backward < 0 || with_backward > LMH_WS_BWD_BF16)
+    return fail(LMH_ERR_ARGS, "with_backward must be 0, 1 or 2, got %d", with_backward);
   size_t b = lmh::plan_forward(N, H, V).bytes;
-  if (with_backward) b = std::max(b, lmh::plan_backward(N, H, V, chunk_size).bytes);
+  if (with_backward) {
+    const lmh::BwdPlan p = lmh::plan_backward(N, H, V, chunk_size);
+    b = std::max(b, with_backward == LMH_WS_BWD_BF16 ? p.bytes_bf16 : p.bytes);
+  }
   *bytes_out = b;
   return ok();
 }
@@ -361,10 +376,11 @@ int lmhead_logps_fwd_noalloc(const uint16_t* hidden, const uint16_t* W, const in
 namespace {
 
 // The backward of W's rows [voff, voff + V) of a vocabulary of Vtot ids.
-int bwd_impl(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, int64_t N, int64_t H,
-             int64_t V, int64_t voff, int64_t Vtot, int64_t chunk_size, float temperature,
-             const float* lse, const float* entropy, const float* g_logp, const float* g_ent, float* dh,
-             float* dW, unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
+// dh / dW are float32 (bf16_out false) or bf16 gradients (bf16_out true).
+int bwd_impl(const char* who, const uint16_t* hidden, const uint16_t* W, const int32_t* targets, int64_t N,
+             int64_t H, int64_t V, int64_t voff, int64_t Vtot, int64_t chunk_size, float temperature,
+             const float* lse, const float* entropy, const float* g_logp, const float* g_ent, void* dh,
+             void* dW, unsigned flags, bool bf16_out, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_shape(N, H, V, chunk_size);
   if (rc != LMH_OK) return rc;
   rc = check_shard(V, voff, Vtot);
@@ -372,34 +388,39 @@ int bwd_impl(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, 
   rc = check_temperature(temperature);
   if (rc != LMH_OK) return rc;
   if (flags & ~(unsigned)(LMH_BWD_ACCUMULATE_DH | LMH_BWD_ACCUMULATE_DW))
-    return fail(LMH_ERR_ARGS, "bwd: unknown flags 0x%x", flags);
+    return fail(LMH_ERR_ARGS, "%s: unknown flags 0x%x", who, flags);
   const bool acc_dh = (flags & LMH_BWD_ACCUMULATE_DH) != 0;
   const bool acc_dW = (flags & LMH_BWD_ACCUMULATE_DW) != 0;
   if (g_ent != nullptr && entropy == nullptr)
-    return fail(LMH_ERR_ARGS, "bwd: g_ent given without the forward's entropy");
-  if (!dW) return fail(LMH_ERR_NULL, "bwd: dW must be non-NULL");
+    return fail(LMH_ERR_ARGS, "%s: g_ent given without the forward's entropy", who);
+  if (!dW) return fail(LMH_ERR_NULL, "%s: dW must be non-NULL", who);
+  if (!aligned(dW, bf16_out ? 16 : 4))
+    return fail(LMH_ERR_UNSUPPORTED, "%s: dW needs %d-byte alignment", who, bf16_out ? 16 : 4);
   rc = check_backward_size(N, V);
   if (rc != LMH_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (N == 0) {
     if (acc_dW) return ok();   // nothing to add
-    const hipError_t e = lmh::launch_fill_zero(dW, V * H, s);
-    if (e != hipSuccess) return fail(LMH_ERR_HIP, "bwd: launch failed: %s", hipGetErrorString(e));
+    // bf16 zeros are 32-bit zeros two at a time (V * H is even: H % 64 == 0)
+    const hipError_t e = lmh::launch_fill_zero(static_cast<float*>(dW), bf16_out ? V * H / 2 : V * H, s);
+    if (e != hipSuccess) return fail(LMH_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
     return ok();
   }
   if (!hidden || !W || !targets || !lse || !dh || !workspace)
-    return fail(LMH_ERR_NULL, "bwd: hidden, W, targets, lse, dh, dW and workspace must be non-NULL");
-  if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(workspace, 16) || !aligned(dh, 16) ||
-      !aligned(dW, 4))
-    return fail(LMH_ERR_UNSUPPORTED, "bwd: hidden, W, dh and workspace need 16-byte alignment");
+    return fail(LMH_ERR_NULL, "%s: hidden, W, targets, lse, dh, dW and workspace must be non-NULL", who);
+  if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(workspace, 16) || !aligned(dh, 16))
+    return fail(LMH_ERR_UNSUPPORTED, "%s: hidden, W, dh and workspace need 16-byte alignment", who);
   const lmh::BwdPlan p = lmh::plan_backward(N, H, V, chunk_size);
-  if (workspace_bytes < p.bytes)
-    return fail(LMH_ERR_WORKSPACE, "bwd: workspace of %zu bytes, %zu needed", workspace_bytes, p.bytes);
+  const size_t need = bf16_out ? p.bytes_bf16 : p.bytes;
+  if (workspace_bytes < need)
+    return fail(LMH_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes, need);
   char* ws = static_cast<char*>(workspace);
   uint16_t* dzbuf[2] = {reinterpret_cast<uint16_t*>(ws), reinterpret_cast<uint16_t*>(ws + p.off_dz1)};
   uint16_t* ht = reinterpret_cast<uint16_t*>(ws + p.off_ht);
   uint16_t* W_tail = reinterpret_cast<uint16_t*>(ws + p.off_tail);
   int* ctr = reinterpret_cast<int*>(ws + p.off_ctr);
+  float* acc_h = reinterpret_cast<float*>(ws + p.off_acc_dh);
+  float* acc_w = reinterpret_cast<float*>(ws + p.off_acc_dW);
   const int64_t v_tail = V / 64 * 64;
   const int64_t nb = p.n_tb * p.n_vb;
   // the cotangent-tile counters start at zero (a fill kernel, not a memset:
@@ -408,7 +429,7 @@ int bwd_impl(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, 
   if (te == hipSuccess)
     te = lmh::launch_transpose(hidden, H, N, H, p.N_pad, p.H_pad, targets, Vtot, ht, p.ld_ht, s);
   if (te == hipSuccess && v_tail < V) te = lmh::launch_pad_rows(W + v_tail * H, V - v_tail, H, 64, W_tail, s);
-  if (te != hipSuccess) return fail(LMH_ERR_HIP, "bwd: launch failed: %s", hipGetErrorString(te));
+  if (te != hipSuccess) return fail(LMH_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(te));
 
   lmh::BwdStep st{};
   st.hidden = hidden;
@@ -429,18 +450,32 @@ int bwd_impl(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, 
   st.ld_ht = p.ld_ht;
   st.W_tail = v_tail < V ? W_tail : nullptr;
   st.v_tail = (int)v_tail;
-  st.dh = dh;
-  st.dW = dW;
+  st.dh = bf16_out ? nullptr : static_cast<float*>(dh);
+  st.dW = bf16_out ? nullptr : static_cast<float*>(dW);
   st.ld_dz = p.ld_dz;
   st.n_ht = (int)lmh::ceil_div(H, lmh::kTileRows);
-  // blocks in a fixed order (token blocks outer, vocabulary blocks inner);
-  // launch j forms block j's cotangent and runs block j-1's GEMMs
+  // blocks in a fixed order: token blocks outer (vocabulary blocks inner),
+  // except for bf16 gradients with N <= V, which run vocabulary blocks outer
+  // so that each vocabulary block's dW is complete (and rounded) before the
+  // next starts. Launch j forms block j's cotangent and runs block j-1's GEMMs.
+  const bool vocab_major = bf16_out && p.vocab_outer;
+  auto block_of = [&](int64_t j, int64_t& tb, int64_t& vb) {
+    if (vocab_major) {
+      vb = j / p.n_tb;
+      tb = j % p.n_tb;
+    } else {
+      tb = j / p.n_vb;
+      vb = j % p.n_vb;
+    }
+  };
+  uint16_t* dh16 = static_cast<uint16_t*>(dh);
+  uint16_t* dW16 = static_cast<uint16_t*>(dW);
   for (int64_t j = 0; j <= nb; ++j) {
     st.z_ctr = ctr + j * 8;
     if (j >= 1) {
-      const int64_t g = j - 1;
-      const int64_t tb = g / p.n_vb, vb = g % p.n_vb;
-      st.g_dz = dzbuf[g & 1];
+      int64_t tb, vb;
+      block_of(j - 1, tb, vb);
+      st.g_dz = dzbuf[(j - 1) & 1];
       st.g_t0 = (int)(tb * p.Ct);
       st.g_Ct = (int)std::min(p.Ct, N - tb * p.Ct);
       st.g_v0 = (int)(vb * p.Vb);
@@ -449,12 +484,33 @@ int bwd_impl(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, 
       st.g_acc_dW = tb > 0 || acc_dW;
       st.n_dw = (int)(lmh::ceil_div(st.g_Vb, lmh::kTileRows) * st.n_ht);
       st.n_dh = (int)(lmh::ceil_div(st.g_Ct, lmh::kTileRows) * st.n_ht);
+      if (bf16_out) {
+        // each gradient sums its blocks in order (dW over token blocks, dh
+        // over vocabulary blocks) in a float32 accumulator; its first block
+        // starts from nothing (or the caller's bf16 values when adding) and
+        // its last writes the caller's bf16 gradient
+        const int64_t t0 = tb * p.Ct, v0 = vb * p.Vb;
+        uint16_t* w_out = dW16 + v0 * H;
+        float* w_acc = p.vocab_outer ? acc_w : acc_w + v0 * H;
+        st.o_dW.src_kind = tb == 0 ? (acc_dW ? lmh::kSrcBf16 : lmh::kSrcNone) : lmh::kSrcF32;
+        st.o_dW.src = tb == 0 ? static_cast<const void*>(w_out) : static_cast<const void*>(w_acc);
+        st.o_dW.dst_bf16 = tb == p.n_tb - 1;
+        st.o_dW.dst = st.o_dW.dst_bf16 ? static_cast<void*>(w_out) : static_cast<void*>(w_acc);
+        uint16_t* h_out = dh16 + t0 * H;
+        float* h_acc = p.vocab_outer ? acc_h + t0 * H : acc_h;
+        st.o_dh.src_kind = vb == 0 ? (acc_dh ? lmh::kSrcBf16 : lmh::kSrcNone) : lmh::kSrcF32;
+        st.o_dh.src = vb == 0 ? static_cast<const void*>(h_out) : static_cast<const void*>(h_acc);
+        st.o_dh.dst_bf16 = vb == p.n_vb - 1;
+        st.o_dh.dst = st.o_dh.dst_bf16 ? static_cast<void*>(h_out) : static_cast<void*>(h_acc);
+        st.dh_dead_zero = st.o_dh.dst_bf16 && !acc_dh;
+      }
     } else {
       st.g_dz = nullptr;
       st.n_dw = st.n_dh = 0;
     }
     if (j < nb) {
-      const int64_t tb = j / p.n_vb, vb = j % p.n_vb;
+      int64_t tb, vb;
+      block_of(j, tb, vb);
       st.z_dz = dzbuf[j & 1];
       st.z_t0 = (int)(tb * p.Ct);
       st.z_Ct = (int)std::min(p.Ct, N - tb * p.Ct);
@@ -466,8 +522,8 @@ int bwd_impl(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, 
       st.z_dz = nullptr;
       st.z_ntt = st.z_nvt = 0;
     }
-    const hipError_t e = lmh::launch_bwd_step(st, s);
-    if (e != hipSuccess) return fail(LMH_ERR_HIP, "bwd: launch failed: %s", hipGetErrorString(e));
+    const hipError_t e = bf16_out ? lmh::launch_bwd_step_bf16(st, s) : lmh::launch_bwd_step(st, s);
+    if (e != hipSuccess) return fail(LMH_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   }
   return ok();
 }
@@ -481,8 +537,16 @@ int lmhead_logps_bwd_ex(const uint16_t* hidden, const uint16_t* W, const int32_t
                         const float* lse, const float* entropy, const float* g_logp,
                         const float* g_ent, float* dh, float* dW, unsigned flags, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  return bwd_impl(hidden, W, targets, N, H, V, 0, V, chunk_size, temperature, lse, entropy, g_logp, g_ent,
-                  dh, dW, flags, workspace, workspace_bytes, stream);
+  return bwd_impl("bwd", hidden, W, targets, N, H, V, 0, V, chunk_size, temperature, lse, entropy, g_logp, g_ent,
+                  dh, dW, flags, false, workspace, workspace_bytes, stream);
+}
+
+int lmhead_logps_bwd_bf16(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, int64_t N,
+                          int64_t H, int64_t V, int64_t chunk_size, float temperature, const float* lse,
+                          const float* entropy, const float* g_logp, const float* g_ent, uint16_t* dh,
+                          uint16_t* dW, unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl("bwd_bf16", hidden, W, targets, N, H, V, 0, V, chunk_size, temperature, lse, entropy, g_logp,
+                  g_ent, dh, dW, flags, true, workspace, workspace_bytes, stream);
 }
 
 int lmhead_logps_bwd_shard(const uint16_t* hidden, const uint16_t* W_shard, const int32_t* targets,
@@ -490,8 +554,9 @@ int lmhead_logps_bwd_shard(const uint16_t* hidden, const uint16_t* W_shard, cons
                            int64_t chunk_size, float temperature, const float* lse, const float* entropy,
                            const float* g_logp, const float* g_ent, float* dh, float* dW_shard,
                            unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(hidden, W_shard, targets, N, H, V_shard, vocab_offset, V_total, chunk_size, temperature,
-                  lse, entropy, g_logp, g_ent, dh, dW_shard, flags, workspace, workspace_bytes, stream);
+  return bwd_impl("bwd_shard", hidden, W_shard, targets, N, H, V_shard, vocab_offset, V_total, chunk_size,
+                  temperature, lse, entropy, g_logp, g_ent, dh, dW_shard, flags, false, workspace, workspace_bytes,
+                  stream);
 }
 
 int lmhead_logps_fwd(const uint16_t* hidden, const uint16_t* W, const int32_t* targets, int64_t N,

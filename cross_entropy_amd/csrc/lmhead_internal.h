@@ -40,6 +40,14 @@ struct BwdPlan {
   size_t off_dz1 = 0, off_ht = 0, off_tail = 0;   // byte offsets in the workspace
   size_t off_ctr = 0;          // 8 int32 cotangent-tile counters per launch (n_tb * n_vb + 1 launches)
   size_t bytes = 0;            // total
+  // bf16-gradient backward: float32 accumulators of the gradients across
+  // blocks. With vocab_outer (N <= V) the blocks run vocabulary-major: dh
+  // accumulates in acc_dh [N_pad][H] over the whole call and each vocabulary
+  // block's dW in acc_dW [Vb][H]; otherwise token-major: dW in acc_dW
+  // [V_pad][H] over the call and each token block's dh in acc_dh [Ct][H].
+  bool vocab_outer = false;
+  size_t off_acc_dh = 0, off_acc_dW = 0;
+  size_t bytes_bf16 = 0;       // total with the accumulators
 };
 
 FwdPlan plan_forward(int64_t N, int64_t H, int64_t V);
@@ -61,6 +69,15 @@ struct FwdArgs {
   float* entropy;
   float* lse;
   float* rec;     // shard partial records [N][4] instead of logp/entropy/lse, or NULL
+};
+
+// Where a gradient tile of the bf16-gradient backward reads and writes.
+enum SrcKind { kSrcNone = 0, kSrcF32 = 1, kSrcBf16 = 2 };
+struct GradOut {
+  const void* src = nullptr;
+  int src_kind = kSrcNone;
+  void* dst = nullptr;
+  int dst_bf16 = 0;
 };
 
 // One backward launch: the gradient tiles of one block (n_dw + n_dh tiles,
@@ -92,10 +109,18 @@ struct BwdStep {
   uint16_t* z_dz;
   int* z_ctr;   // this launch's 8 per-XCD tile counters (zero before the launch)
   int z_t0, z_Ct, z_v0, z_Vb, z_ntt, z_nvt;
+  // bf16-gradient backward only (bwd_step_bf16_kernel): per gradient, where
+  // this block's tiles read the values they add to (none, a float32
+  // accumulator or the caller's bf16 gradient) and where they write the sum
+  // (a float32 accumulator, or the caller's bf16 gradient, rounded once),
+  // both pointing at the block's first row (row stride H). Masked tokens'
+  // dh rows are stored as 0 when dh_dead_zero, else left as they are.
+  GradOut o_dh, o_dW;
+  int dh_dead_zero;
 };
 
 // Kernel ids of the tracing facility (lmhead_trace.hip).
-enum KernelId { kFwdStats = 0, kFwdMerge, kBwdStep, kTranspose, kFill, kPadRows, kNumKernels };
+enum KernelId { kFwdStats = 0, kFwdMerge, kBwdStep, kTranspose, kFill, kPadRows, kBwdStepBf16, kNumKernels };
 void trace_begin(hipStream_t stream);
 void trace_end(int kernel, hipStream_t stream, double flops, double bytes);
 
@@ -104,6 +129,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_merge(const float* partials, int P, int64_t N, const int32_t* targets, int64_t Vtot,
                         float invT, float* logp, float* entropy, float* lse, hipStream_t stream);
 hipError_t launch_bwd_step(const BwdStep& st, hipStream_t stream);
+hipError_t launch_bwd_step_bf16(const BwdStep& st, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_pad_rows(const uint16_t* in, int64_t R, int64_t C, int64_t R_pad, uint16_t* out,
                            hipStream_t stream);

@@ -869,8 +869,133 @@ __device__ __forceinline__ void write_acc(float* __restrict__ out, int64_t ld, i
   }
 }
 
+// The bf16-gradient backward's writers: the same tile layouts as write_acc
+// (dW, row-major) and write_acc_t (dh, transposed), reading the values to add
+// to from o.src (nothing, a float32 accumulator or a bf16 gradient, widened)
+// and writing the sum to o.dst (a float32 accumulator, or a bf16 gradient,
+// rounded to nearest even once). Both descriptors point at row 0 of the
+// block; rows have stride ld.
+__device__ __forceinline__ float widen_bf16(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ uint16_t round_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+__device__ __forceinline__ void write_acc_g(const GradOut& o, int64_t ld, int r_base, int rows, int c_base,
+                                            int cols, f32x4 (&acc)[kNB][kNB]) {
+  const int lane = threadIdx.x & 63;
+  const float* sf = static_cast<const float*>(o.src);
+  const uint16_t* sb = static_cast<const uint16_t*>(o.src);
+  float* df = static_cast<float*>(o.dst);
+  uint16_t* db = static_cast<uint16_t*>(o.dst);
+  bool col_ok[kNB];
+  int col[kNB];
+#pragma unroll
+  for (int j = 0; j < kNB; ++j) {
+    const int c = c_base + j * 16 + (lane & 15);
+    col_ok[j] = c < cols;
+    col[j] = col_ok[j] ? c : cols - 1;
+  }
+#pragma unroll
+  for (int i = 0; i < kNB; ++i) {
+    float old[4][kNB];
+    bool row_ok[4];
+    int row[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = r_base + acc_row(i, r, lane);
+      row_ok[r] = m < rows;
+      row[r] = row_ok[r] ? m : rows - 1;
+    }
+    if (o.src_kind == kSrcF32) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) old[r][j] = sf[(int64_t)row[r] * ld + col[j]];
+    } else if (o.src_kind == kSrcBf16) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) old[r][j] = widen_bf16(sb[(int64_t)row[r] * ld + col[j]]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) old[r][j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) {
+      pin_acc(acc[i][j]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (!(row_ok[r] && col_ok[j])) continue;
+        const float v = old[r][j] + acc[i][j][r];
+        const int64_t at = (int64_t)row[r] * ld + col[j];
+        if (o.dst_bf16) db[at] = round_bf16(v);
+        else df[at] = v;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+__device__ __forceinline__ void write_acc_tg(const GradOut& o, int64_t ld, int r_base, int rows, int c_base,
+                                             int cols, bool dead_zero, const int32_t* __restrict__ targets,
+                                             int t_base, int Vtot, f32x4 (&acc)[kNB][kNB]) {
+  const int lane = threadIdx.x & 63;
+  int col[kNB], tgt[kNB];
+#pragma unroll
+  for (int j = 0; j < kNB; ++j) {
+    const int c = c_base + j * 16 + (lane & 15);
+    col[j] = c < cols ? c : cols - 1;
+    tgt[j] = targets[t_base + col[j]];
+    if (c >= cols) tgt[j] = -2;   // not stored
+  }
+  const int r0 = (r_base < rows ? r_base : 0) + 4 * (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < kNB; ++j) {
+    const bool in = tgt[j] != -2;
+    const bool live = (tgt[j] >= 0) && (tgt[j] < Vtot);
+    const int64_t base = (int64_t)col[j] * ld + r0;
+    f32x4 old[kNB];
+    if (o.src_kind == kSrcF32) {
+      const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(o.src) + base);
+#pragma unroll
+      for (int i = 0; i < kNB; ++i) old[i] = p[r_base + 16 * i < rows ? 4 * i : 0];
+    } else if (o.src_kind == kSrcBf16) {
+      const uint2* p = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(o.src) + base);
+#pragma unroll
+      for (int i = 0; i < kNB; ++i) {
+        const uint2 w = p[r_base + 16 * i < rows ? 4 * i : 0];
+        old[i] = f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kNB; ++i) old[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) {
+      pin_acc(acc[i][j]);
+      if (!(r_base + 16 * i < rows) || !in) continue;
+      if (!live && !dead_zero) continue;
+      const f32x4 v = live ? old[i] + acc[i][j] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (o.dst_bf16) {
+        uint2 w;
+        w.x = pack_bf16x2(v[0], v[1]);
+        w.y = pack_bf16x2(v[2], v[3]);
+        reinterpret_cast<uint2*>(static_cast<uint16_t*>(o.dst) + base)[4 * i] = w;
+      } else {
+        reinterpret_cast<f32x4*>(static_cast<float*>(o.dst) + base)[4 * i] = v;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // dW tile: dW[v0 + m][n] (+)= sum_k dz[k][m] ht[n][t0 + k] over the block's
 // tokens (A = dz read MN-contiguous, B = hidden^T with masked tokens zeroed).
+// BF16: the bf16-gradient backward's writer (s.o_dW).
+template <bool BF16>
 __device__ __forceinline__ void dw_tile(const BwdStep& s, int vid, char* lds) {
   int mt, hb;
   raster(vid, s.n_dw / s.n_ht, s.n_ht, 4, mt, hb);
@@ -885,8 +1010,12 @@ __device__ __forceinline__ void dw_tile(const BwdStep& s, int vid, char* lds) {
   f32x4 acc[kNB][kNB];
   Pipe pipe;
   mma_tile<true, 64>(oa, ob, (s.g_Ct + kBK - 1) / kBK * kBK, lds, acc, pipe, oa.base, ob.base, false);
-  write_acc(s.dW + (int64_t)s.g_v0 * H, H, m0 + wm * 128, s.g_Vb, h0 + wn * 128, H, s.g_acc_dW != 0,
-            nullptr, 0, 0, acc);
+  if constexpr (BF16) {
+    write_acc_g(s.o_dW, H, m0 + wm * 128, s.g_Vb, h0 + wn * 128, H, acc);
+  } else {
+    write_acc(s.dW + (int64_t)s.g_v0 * H, H, m0 + wm * 128, s.g_Vb, h0 + wn * 128, H, s.g_acc_dW != 0,
+              nullptr, 0, 0, acc);
+  }
 }
 
 // Write one wave's 128 x 128 accumulator block transposed: element (row,
@@ -941,7 +1070,9 @@ __device__ __forceinline__ void write_acc_t(float* __restrict__ out, int64_t ld,
 // over the block's vocabulary (A = W as it lies, MN-contiguous, B = the
 // cotangent rows); masked token rows are written as 0 (left alone when
 // adding). W's rows past V in the block's last slice are read from the
-// zero-padded copy of its last rows.
+// zero-padded copy of its last rows. BF16: the bf16-gradient backward's
+// writer (s.o_dh).
+template <bool BF16>
 __device__ __forceinline__ void dh_tile(const BwdStep& s, int vid, char* lds) {
   int mt, hb;
   raster(vid, s.n_dh / s.n_ht, s.n_ht, 4, mt, hb);
@@ -958,8 +1089,13 @@ __device__ __forceinline__ void dh_tile(const BwdStep& s, int vid, char* lds) {
   f32x4 acc[kNB][kNB];
   Pipe pipe;
   mma_tile<true, 64>(oa, ob, (s.g_Vb + kBK - 1) / kBK * kBK, lds, acc, pipe, oa.base, ob.base, false);
-  write_acc_t(s.dh + (int64_t)s.g_t0 * H, H, h0 + wm * 128, H, m0 + wn * 128, s.g_Ct, s.g_acc_dh != 0,
-              s.targets, s.g_t0, s.Vtot, acc);
+  if constexpr (BF16) {
+    write_acc_tg(s.o_dh, H, h0 + wm * 128, H, m0 + wn * 128, s.g_Ct, s.dh_dead_zero != 0, s.targets, s.g_t0,
+                 s.Vtot, acc);
+  } else {
+    write_acc_t(s.dh + (int64_t)s.g_t0 * H, H, h0 + wm * 128, H, m0 + wn * 128, s.g_Ct, s.g_acc_dh != 0,
+                s.targets, s.g_t0, s.Vtot, acc);
+  }
 }
 
 // One backward launch: each XCD (workgroups are dealt to the 8 XCDs
@@ -980,9 +1116,8 @@ constexpr int kStealSlots = 32;   // one round of the XCD's 32 CUs
 
 __device__ __forceinline__ int z_share_lo(int x, int n_z) { return x * n_z / 8; }
 
-__global__ __launch_bounds__(kThreads) void bwd_step_kernel(const BwdStep s) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  __shared__ int z_tile;
+template <bool BF16>
+__device__ __forceinline__ void bwd_step(const BwdStep& s, char* lds, int& z_tile) {
   const int xcd = blockIdx.x & 7;
   const int loc = blockIdx.x >> 3;
   const int n_z = s.z_ntt * s.z_nvt;
@@ -996,9 +1131,9 @@ __global__ __launch_bounds__(kThreads) void bwd_step_kernel(const BwdStep s) {
   if (loc < g_cnt) {
     const bool is_dh = (loc < first_cnt) == dh_first;
     if (is_dh) {
-      dh_tile(s, dh_lo + (dh_first ? loc : loc - dw_cnt), lds);
+      dh_tile<BF16>(s, dh_lo + (dh_first ? loc : loc - dw_cnt), lds);
     } else {
-      dw_tile(s, dw_lo + (dh_first ? loc - dh_cnt : loc), lds);
+      dw_tile<BF16>(s, dw_lo + (dh_first ? loc - dh_cnt : loc), lds);
     }
     return;
   }
@@ -1018,6 +1153,19 @@ __global__ __launch_bounds__(kThreads) void bwd_step_kernel(const BwdStep s) {
   __syncthreads();
   const int tile = z_tile;
   if (tile >= 0) dz_tile(s, tile, lds);
+}
+
+__global__ __launch_bounds__(kThreads) void bwd_step_kernel(const BwdStep s) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  __shared__ int z_tile;
+  bwd_step<false>(s, lds, z_tile);
+}
+
+// The same launch writing bf16 gradients through float32 accumulators.
+__global__ __launch_bounds__(kThreads) void bwd_step_bf16_kernel(const BwdStep s) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  __shared__ int z_tile;
+  bwd_step<true>(s, lds, z_tile);
 }
 
 // Transposed bf16 copy: out[c][r] = in[r][c] for r < R and c < C, 0 for the
@@ -1127,7 +1275,8 @@ hipError_t launch_merge(const float* partials, int P, int64_t N, const int32_t* 
   return hipSuccess;
 }
 
-hipError_t launch_bwd_step(const BwdStep& st, hipStream_t stream) {
+template <bool BF16>
+static hipError_t launch_bwd(const BwdStep& st, hipStream_t stream) {
   const int n_z = st.z_ntt * st.z_nvt;
   int per = 0;
   for (int x = 0; x < 8; ++x)
@@ -1139,7 +1288,8 @@ hipError_t launch_bwd_step(const BwdStep& st, hipStream_t stream) {
   const double gc = (double)st.g_Ct, gv = (double)st.g_Vb;
   const double zc = (double)st.z_Ct, zv = (double)st.z_Vb;
   trace_begin(stream);
-  hipLaunchKernelGGL(bwd_step_kernel, dim3(8 * per), dim3(kThreads), 0, stream, st);
+  if (BF16) hipLaunchKernelGGL(bwd_step_bf16_kernel, dim3(8 * per), dim3(kThreads), 0, stream, st);
+  else hipLaunchKernelGGL(bwd_step_kernel, dim3(8 * per), dim3(kThreads), 0, stream, st);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // algorithmic (credited) work: 2 Ct Vb H for each of the dh and dW GEMMs;
@@ -1149,9 +1299,12 @@ hipError_t launch_bwd_step(const BwdStep& st, hipStream_t stream) {
   const double by = (n_g ? 2.0 * gc * gv + 2.0 * (gc + gv) * H +
                                4.0 * H * (gc * (1 + st.g_acc_dh) + gv * (1 + st.g_acc_dW)) : 0.0) +
                     (n_z ? 2.0 * zc * zv + 2.0 * (zc + zv) * H + 20.0 * zc : 0.0);
-  trace_end(kBwdStep, stream, fl, by);
+  trace_end(BF16 ? kBwdStepBf16 : kBwdStep, stream, fl, by);
   return hipSuccess;
 }
+
+hipError_t launch_bwd_step(const BwdStep& st, hipStream_t stream) { return launch_bwd<false>(st, stream); }
+hipError_t launch_bwd_step_bf16(const BwdStep& st, hipStream_t stream) { return launch_bwd<true>(st, stream); }
 
 hipError_t launch_transpose(const uint16_t* in, int64_t ld_in, int64_t R, int64_t C, int64_t R_pad,
                             int64_t C_pad, const int32_t* tgt, int64_t V, uint16_t* out,

@@ -39,7 +39,7 @@ thread_local hipEvent_t t_start = nullptr;
 
 const char* const kNames[kNumKernels] = {
     "fwd_stats_kernel", "fwd_merge_kernel", "bwd_step_kernel", "transpose_kernel", "fill_zero_kernel",
-    "pad_rows_kernel",
+    "pad_rows_kernel", "bwd_step_bf16_kernel",
 };
 
 hipEvent_t take_event() {

@@ -102,15 +102,19 @@ extern "C" {
 #define LMH_ERR_HIP (-7)         /* a HIP call or kernel launch failed */
 
 /*
- * Bytes of device workspace a call needs. with_backward = 0 sizes the
- * forward only; with_backward != 0 sizes a workspace that serves both the
- * forward and the backward (one buffer may be reused for both calls when
- * they run in stream order). Pure host computation, no device call.
- * Errors: LMH_ERR_NULL (bytes_out), LMH_ERR_SHAPE, LMH_ERR_CHUNK,
- * LMH_ERR_UNSUPPORTED (with_backward and N or V above 2^23 - 256: the
- * backward addresses 256-row tiles of its transposed operands with 32-bit
- * offsets).
+ * Bytes of device workspace a call needs. with_backward = LMH_WS_FWD (0)
+ * sizes the forward only; LMH_WS_BWD (1) sizes a workspace that serves both
+ * the forward and the float32-gradient backward (one buffer may be reused
+ * for both calls when they run in stream order); LMH_WS_BWD_BF16 (2) sizes
+ * one that also serves lmhead_logps_bwd_bf16. Pure host computation, no
+ * device call. Errors: LMH_ERR_NULL (bytes_out), LMH_ERR_SHAPE,
+ * LMH_ERR_CHUNK, LMH_ERR_ARGS (with_backward not 0, 1 or 2),
+ * LMH_ERR_UNSUPPORTED (a backward with N or V above 2^23 - 256: the backward
+ * addresses 256-row tiles of its transposed operands with 32-bit offsets).
  */
+#define LMH_WS_FWD 0
+#define LMH_WS_BWD 1
+#define LMH_WS_BWD_BF16 2
 int lmhead_logps_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t chunk_size,
                                  int with_backward, size_t* bytes_out);
 
@@ -208,6 +212,32 @@ int lmhead_logps_bwd_ex(const uint16_t* hidden, const uint16_t* W, const int32_t
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward writing bf16 gradients (a trainer whose parameters and
+ * activations are bf16 takes the head's gradients in their own dtype;
+ * tunix #2913 hands the head's gradients to the trainer's own
+ * accumulation). The computation of lmhead_logps_bwd_ex, with
+ *   dh  bf16 [N, H]   out (masked rows 0), or added into with
+ *                     LMH_BWD_ACCUMULATE_DH (masked rows unchanged)
+ *   dW  bf16 [V, H]   out, or added into with LMH_BWD_ACCUMULATE_DW
+ * both 16-byte aligned. Each gradient element is summed over the blocks in
+ * float32 inside the workspace, in the same order as the float32 backward,
+ * and rounded to bf16 (nearest even) once, when its last block is added: the
+ * result is the float32 backward's rounded to bf16, bit for bit (with an
+ * ACCUMULATE flag, the previous bf16 value widened to float32 is the sum's
+ * starting value). Workspace: lmhead_logps_workspace_bytes(...,
+ * LMH_WS_BWD_BF16) bytes, the float32 backward's plus float32 accumulators
+ * of min(N, V) x H elements (the smaller gradient, summed over the whole
+ * call) and of one block's rows of the other. Everything else (arguments,
+ * errors, N = 0, stream semantics) is that of lmhead_logps_bwd_ex.
+ */
+int lmhead_logps_bwd_bf16(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
+                          int64_t N, int64_t H, int64_t V, int64_t chunk_size, float temperature,
+                          const float* lse, const float* entropy,
+                          const float* g_logp, const float* g_ent,
+                          uint16_t* dh, uint16_t* dW, unsigned flags,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Vocabulary shards (tunix #2913's head runs sharded, its vocabulary table
  * split across devices, the per-token (max, exp-sum) partials combined across
  * shards; the same log-sum-exp combination as blockwise attention's, palingenesis
@@ -287,6 +317,7 @@ const char* lmhead_logps_version(void);
  *   3 transpose_kernel  (bf16 transpose of the hidden states)
  *   4 fill_zero_kernel
  *   5 pad_rows_kernel   (W's last V % 64 rows, zero-padded to 64)
+ *   6 bwd_step_bf16_kernel (bwd_step_kernel writing bf16 gradients)
  * lmhead_logps_trace_enable(on) clears the totals and starts (on != 0) or
  * stops recording. lmhead_logps_trace_read(kernel, ...) waits for the
  * recorded launches to finish and returns, for that kernel, the launch

@@ -287,3 +287,45 @@ def test_noalloc_scratch_size_matches_header_and_rejects_large_calls():
     assert nat.raw_fwd_noalloc(**dict(a, H=100)) == -6
     assert nat.raw_fwd_noalloc(**dict(a, temperature=0.0)) == -5
     assert nat.raw_fwd_noalloc(**dict(a, N=0)) == 0
+
+
+def _bwd16(**kw):
+    a = dict(hidden=FAKE, W=FAKE, targets=FAKE, N=64, H=128, V=300, chunk_size=16, temperature=1.0, lse=FAKE,
+             entropy=FAKE, g_logp=FAKE, g_ent=FAKE, dh=FAKE, dW=FAKE, flags=0, workspace=FAKE, workspace_bytes=0,
+             stream=0)
+    a.update(kw)
+    return nat.raw_bwd_bf16(**a)
+
+
+def test_bf16_backward_argument_errors():
+    """The bf16-gradient backward's host checks: the backward's codes, its
+    own workspace size (the float32 backward's plus its accumulators) and
+    16-byte aligned bf16 gradients."""
+    assert _bwd16(N=-1) == -2
+    assert _bwd16(chunk_size=0) == -3
+    assert _bwd16(flags=4) == -5
+    assert _bwd16(entropy=0) == -5
+    assert _bwd16(dW=0) == -1
+    assert _bwd16(dW=MIS) == -6
+    assert _bwd16(dh=MIS) == -6
+    f32 = nat.raw_workspace_bytes(64, 128, 300, 16, nat.WS_BWD)
+    b16 = nat.raw_workspace_bytes(64, 128, 300, 16, nat.WS_BWD_BF16)
+    assert b16 > f32
+    assert _bwd16(workspace_bytes=f32) == -4
+    assert "bwd_bf16" in nat.load().lmhead_logps_last_error().decode()
+    with pytest.raises(nat.LmheadError):
+        nat.raw_workspace_bytes(64, 128, 300, 16, 3)
+
+
+@pytest.mark.parametrize("N,H,V,C", [(65536, 2560, 151936, 512), (4096, 2560, 151936, 512), (200000, 256, 5000, 64)])
+def test_bf16_workspace_holds_the_smaller_gradient_in_float32(N, H, V, C):
+    """The bf16 backward's extra workspace: min(N, V) x H float32 (the
+    smaller gradient summed over the call) plus one block's rows of the other,
+    never a float32 copy of both gradients."""
+    f32 = nat.raw_workspace_bytes(N, H, V, C, nat.WS_BWD)
+    b16 = nat.raw_workspace_bytes(N, H, V, C, nat.WS_BWD_BF16)
+    extra = b16 - f32
+    whole = 4 * (-(-min(N, V) // 256) * 256) * H
+    # a block edge is at most chunk_size * V / 256 (blocks hold at most chunk_size * V elements, edges >= 256)
+    assert whole <= extra <= whole + 4 * H * (C * V // 256 + 256) + 512, (extra, whole)
+
