@@ -1,10 +1,18 @@
 """Builds the HIP library ``liblmhead_logps.so`` in-tree for gfx950.
 
-    python -m cross_entropy_amd.build        (from the repository root)
+    python -m cross_entropy_amd.build             (from the repository root)
+    python -m cross_entropy_amd.build --sanitize  (host ASan + UBSan build)
 
 Every call compiles from source (no cache). The library holds the kernels
 and the C ABI of ``include/lmhead_logps.h``; the Python binding loads it
 from this directory.
+
+``--sanitize`` builds ``liblmhead_logps_sanitize.so`` with AddressSanitizer
+and UndefinedBehaviorSanitizer on the host code only (argument checks, the
+planner, workspace layout, tracing; the device code is built as usual). The
+host tests run against it with the ASan runtime preloaded and
+``LMHEAD_LOGPS_LIB`` pointing the binding at it; ``sanitizer_env()`` gives
+that environment.
 """
 from __future__ import annotations
 
@@ -42,10 +50,48 @@ def hipcc() -> str:
     return path
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library and return its path. Raises on failure."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc()] + HIP_FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+SANITIZE_LIB_PATH = os.path.join(PKG, "liblmhead_logps_sanitize.so")
+# host-only sanitizers: each -fsanitize= applies to the host compilation
+SANITIZE_FLAGS = [
+    "-Xarch_host", "-g", "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+]
+
+
+def asan_runtime() -> str:
+    """The clang ASan runtime matching hipcc's host compiler."""
+    out = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = out.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        import glob
+        found = sorted(glob.glob("/opt/rocm*/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+        if not found:
+            raise RuntimeError("libclang_rt.asan-x86_64.so not found")
+        path = found[-1]
+    return path
+
+
+def sanitizer_env() -> dict:
+    """Environment for a host process that loads the sanitizer build."""
+    env = dict(os.environ)
+    env["LD_PRELOAD"] = asan_runtime()
+    env["LMHEAD_LOGPS_LIB"] = SANITIZE_LIB_PATH
+    # the Python interpreter itself is not instrumented; its allocations are
+    # not leaks of the library
+    env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1"
+    env["UBSAN_OPTIONS"] = "print_stacktrace=1:halt_on_error=1"
+    return env
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile the library (or its host-sanitized variant) and return its
+    path. Raises on failure."""
+    out = SANITIZE_LIB_PATH if sanitize else LIB_PATH
+    tmp = out + ".tmp"
+    flags = HIP_FLAGS + (SANITIZE_FLAGS if sanitize else [])
+    cmd = [hipcc()] + flags + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,9 +102,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:]))

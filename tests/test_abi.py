@@ -329,3 +329,23 @@ def test_bf16_workspace_holds_the_smaller_gradient_in_float32(N, H, V, C):
     # a block edge is at most chunk_size * V / 256 (blocks hold at most chunk_size * V elements, edges >= 256)
     assert whole <= extra <= whole + 4 * H * (C * V // 256 + 256) + 512, (extra, whole)
 
+
+def test_planner_sweep_sizes():
+    """Workspace sizes over a sweep of shapes, chunk sizes and the three
+    kinds (run under the host sanitizers by tests/test_sanitize.py, where
+    any overflow in the planner's arithmetic aborts): sizes are positive,
+    grow with the kind, and the backward's stays below the float32 chunk
+    bound plus the input-sized parts."""
+    for N in (1, 7, 255, 256, 257, 4096, 65536, 1 << 22, (1 << 23) - 257):
+        for H in (64, 2560, 4096):
+            for V in (1, 5, 4097, 151936, 248320, (1 << 23) - 257):
+                for C in (1, 512, 4096, 1 << 30):
+                    f = nat.raw_workspace_bytes(N, H, V, C, nat.WS_FWD)
+                    b = nat.raw_workspace_bytes(N, H, V, C, nat.WS_BWD)
+                    b16 = nat.raw_workspace_bytes(N, H, V, C, nat.WS_BWD_BF16)
+                    assert 0 < f <= b < b16, (N, H, V, C)
+                    n_pad, v_pad, h_pad = -(-N // 256) * 256, -(-V // 256) * 256, -(-H // 256) * 256
+                    # two bf16 cotangent buffers within max(chunk * V, one tile), hidden^T, W tail, counters
+                    dz = 4 * min(max(C * V, 256 * 320), n_pad * (v_pad + 128)) + 4 * 64 * max(n_pad, v_pad)
+                    ht = 2 * h_pad * (n_pad + 128)
+                    assert b <= max(f, dz + ht + 2 * 64 * H + 8 * 4 * 8192 * 64 + 4096), (N, H, V, C, b)
