@@ -46,19 +46,49 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def stored_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known size), or
-    None when the counters were taken on another version of the kernels."""
+def stored_counters():
+    """The committed counter summary (FETCH_SIZE / WRITE_SIZE passes, each
+    scaled by a plain copy of known size), or None when the counters were
+    taken on another version of the kernels."""
     path = os.path.join(ROOT, "profiles", "lmhead_traffic_headline.json")
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel") != kernel or t.get("kernels_source_sha256") != kernel_source_hash():
+    if t.get("kernels_source_sha256") != kernel_source_hash():
+        return None
+    return t
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None."""
+    t = stored_counters()
+    if t is None or t.get("kernel") != kernel:
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def w_stream(fwd_ms: float):
+    """The forward's W stream from the committed counter passes (bytes fetched
+    from beyond L2 per forward: a counted bracket and the schedule's figure),
+    as GB/s over this run's forward time and as re-reads of the table."""
+    t = stored_counters()
+    if t is None or "w_stream" not in t:
+        return None
+    w = t["w_stream"]
+    sec = fwd_ms * 1e-3
+    return {
+        "unit": "GB/s",
+        "bytes_per_forward": [w["w_bytes_lower"], w["w_bytes_upper"]],
+        "bytes_per_forward_schedule": w["w_bytes_model"],
+        "achieved": [round(w["w_bytes_lower"] / sec / 1e9, 1), round(w["w_bytes_upper"] / sec / 1e9, 1)],
+        "peak": PEAK_HBM_GBS,
+        "reuse_vs_table": [round(w["w_bytes_lower"] / w["w_table_bytes"], 1),
+                           round(w["w_bytes_upper"] / w["w_table_bytes"], 1)],
+        "forward_fetch_bytes": t.get("fwd_stats_kernel_bytes_per_launch"),
+        "note": "L2-to-fabric fetch (FETCH_SIZE); Infinity Cache hits are included, so HBM reads are at most this",
+    }
 
 
 def cpu_baseline(h_bits, W_bits, targets, chunk, g_l, g_e, sample: int, N: int):
@@ -242,6 +272,7 @@ def main() -> int:
         "kernels": {k: {"launches": v["launches"] // args.steps, "ms_per_step": round(v["ms"] / args.steps, 3)}
                     for k, v in kernels.items() if v["launches"]},
         "traced_ms_per_step": round(traced_elapsed * 1e3 / args.steps, 3),
+        "w_stream": w_stream(fwd_ms) if args.workload == WORKLOAD_INDEX else None,
     }
     if args.no_cpu_baseline:
         out["cpu_baseline"] = None
