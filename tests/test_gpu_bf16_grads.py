@@ -165,3 +165,34 @@ def test_bf16_no_tokens():
     lm.lmhead_logps_bwd_bf16(hd, Wd, td, 8, 1.0, z, None, z, None, dh, dW, 0, ws)
     torch.cuda.synchronize()
     assert bool((dW == 0.0).all())
+
+
+def test_bf16_backward_in_a_hip_graph():
+    """The forward and the bf16 backward captured into one HIP graph and
+    replayed three times: every replay gives the eager run's bits."""
+    import torch
+    import cross_entropy_amd as lm
+    h, W, t, g_l, g_e = _case(15, 1300, 256, 4100, n_masked=9)
+    hd, Wd, td, gl, ge = dev_bits(h), dev_bits(W), dev(t), dev(g_l), dev(g_e)
+    N, H = h.shape
+    V = W.shape[0]
+    ws = lm.workspace_for(hd, Wd, 96, with_backward="bf16")
+    logp, ent, lse = lm.forward(hd, Wd, td, 96, workspace=ws)
+    dh, dW = lm.backward(hd, Wd, td, 96, lse, ent, gl, ge, workspace=ws, grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = [x.view(torch.int16).cpu().numpy().copy() for x in (dh, dW)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    log("[bf16] graph capture")
+    with torch.cuda.graph(g, stream=side):
+        lm.lmhead_logps_fwd(hd, Wd, td, 96, logp, ent, lse, ws)
+        lm.lmhead_logps_bwd_bf16(hd, Wd, td, 96, 1.0, lse, ent, gl, ge, dh, dW, 0, ws)
+    for rep in range(3):
+        dh.fill_(float("nan"))
+        dW.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, x, r in (("dh", dh, ref[0]), ("dW", dW, ref[1])):
+            assert np.array_equal(x.view(torch.int16).cpu().numpy(), r), (rep, name)

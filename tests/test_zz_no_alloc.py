@@ -78,3 +78,39 @@ def test_noalloc_rejects_beyond_its_scratch():
     assert e.value.code == -4
     torch.cuda.synchronize()
     assert bool((logp == 3.0).all()) and bool((lse == 3.0).all())
+
+
+def test_noalloc_forward_in_a_hip_graph():
+    """The use it exists for: captured into a HIP graph (after one eager call,
+    which looks its scratch address up), replayed several times with eager
+    work and synchronisations between the replays; every replay gives the
+    eager call's bits, also after a larger call has used the scratch."""
+    import torch
+    import cross_entropy_amd as lm
+    h_bits, W_bits, t = _inputs(73, 1500, 256, 4100, 11)
+    h, W, tt = dev_bits(h_bits), dev_bits(W_bits), dev(t)
+    N = t.size
+    logp = torch.empty(N, device="cuda")
+    ent = torch.empty(N, device="cuda")
+    lse = torch.empty(N, device="cuda")
+    lm.lmhead_logps_fwd_noalloc(h, W, tt, 512, 0.7, logp, ent, lse)
+    torch.cuda.synchronize()
+    ref = [x.cpu().numpy().copy() for x in (logp, ent, lse)]
+    big = _inputs(74, 9000, 256, 5003, 40)
+    bh, bW, bt = dev_bits(big[0]), dev_bits(big[1]), dev(big[2])
+    bl, be, bs = (torch.empty(9000, device="cuda") for _ in range(3))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    log("[noalloc] graph capture")
+    with torch.cuda.graph(g, stream=side):
+        lm.lmhead_logps_fwd_noalloc(h, W, tt, 512, 0.7, logp, ent, lse)
+    for rep in range(3):
+        for x in (logp, ent, lse):
+            x.fill_(float("nan"))
+        lm.lmhead_logps_fwd_noalloc(bh, bW, bt, 64, 1.0, bl, be, bs)   # other contents in the scratch
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, x, r in zip(("logp", "entropy", "lse"), (logp, ent, lse), ref):
+            assert np.array_equal(x.cpu().numpy(), r), (rep, name)
