@@ -196,3 +196,40 @@ def test_bf16_backward_in_a_hip_graph():
         torch.cuda.synchronize()
         for name, x, r in (("dh", dh, ref[0]), ("dW", dW, ref[1])):
             assert np.array_equal(x.view(torch.int16).cpu().numpy(), r), (rep, name)
+
+
+def test_autograd_memory_at_the_one_sequence_shape():
+    """Between forward and backward the autograd front end holds the outputs,
+    lse and nothing backward-sized (the forward's workspace is the split
+    records only); the backward's peak allocation stays below what a float32
+    dW [V, H] alone would take (1.56 GB here): the bf16 backward's float32
+    accumulators cover min(N, V) x H plus one block's rows, and the gradients
+    are bf16 from the start."""
+    import torch
+    import cross_entropy_amd as lm
+    cfg = WORKLOADS[2]
+    h, W, t = make_inputs(cfg)
+    g_l, g_e = make_cotangents(cfg)
+    N, H, V, C = cfg.N, cfg.H, cfg.V, cfg.chunk_size
+    hd = dev_bits(h).view(torch.bfloat16).clone().requires_grad_(True)
+    Wd = dev_bits(W).view(torch.bfloat16).clone().requires_grad_(True)
+    td, gl, ge = dev(t), dev(g_l), dev(g_e)
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    logp, ent = lm.lmhead_logps(hd, Wd, td, C)
+    loss = (logp * gl).sum() + (ent * ge).sum()
+    torch.cuda.synchronize()
+    held = torch.cuda.memory_allocated() - base
+    log(f"[bf16] autograd: held between forward and backward {held / 1e6:.1f} MB")
+    assert held < 16 * N + (8 << 20), "only per-token outputs and lse are held"
+    torch.cuda.reset_peak_memory_stats()
+    before = torch.cuda.memory_allocated()
+    loss.backward()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - before
+    f32_dW = 4 * V * H
+    ws = lm.lmhead_logps_workspace_bytes(N, H, V, C, with_backward="bf16")
+    log(f"[bf16] autograd: backward peak {peak / 1e6:.1f} MB (workspace {ws / 1e6:.1f} MB, f32 dW {f32_dW / 1e6:.1f} MB)")
+    assert peak < f32_dW, "no float32 [V, H] gradient"
+    assert peak <= ws + 2 * (N + V) * H + (64 << 20)
+    assert hd.grad.dtype == torch.bfloat16 and Wd.grad.dtype == torch.bfloat16
