@@ -119,6 +119,22 @@ def cpu_baseline(h_bits, W_bits, targets, chunk, g_l, g_e, sample: int, N: int):
     }
 
 
+def smi_power():
+    """Board power and per-XCD graphics clocks from one `amd-smi metric`
+    reading (a child process), or None where the tool is unavailable."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--power", "--clock", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        d = json.loads(r.stdout)
+        g = d["gpu_data"][0] if isinstance(d, dict) and "gpu_data" in d else d[0]
+        clk = g["clock"]
+        xcd = [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("gfx_") and isinstance(clk[k].get("clk"), dict)]
+        return {"socket_power_W": g["power"]["socket_power"]["value"], "gfx_clock_MHz": xcd}
+    except Exception as e:  # the tool is absent or printed something else
+        return {"error": repr(e)[:200]}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +146,9 @@ def main() -> int:
                     help="synthetic workload (default 3, the batch-16 x 4096 headline; the others are "
                          "the one-sequence head, the context-rank share and the pad-first packed row)")
     ap.add_argument("--chunk", type=int, default=0, help="chunk_size override (workload 4 runs 1024 and 4096)")
+    ap.add_argument("--power", action="store_true",
+                    help="also read board power and XCD clocks (amd-smi) while the forward alone, then the "
+                         "backward alone, run back to back for a few seconds each")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times), the known-size "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -279,6 +298,20 @@ def main() -> int:
     else:
         log(f"[bench] CPU oracle on {args.cpu_sample} sampled tokens")
         out["cpu_baseline"] = cpu_baseline(h_bits, W_bits, targets, C, g_l, g_e, args.cpu_sample, N)
+    if args.power:
+        # enough queued calls of one kind to keep the GPU busy past the reading
+        torch.cuda.synchronize()
+        time.sleep(1.0)
+        out["power"] = {"idle": smi_power()}
+        for kind, reps in (("forward", 120), ("backward", 40)):
+            for _ in range(reps):
+                if kind == "forward":
+                    lm.lmhead_logps_fwd(h, W, t, C, logp, ent, lse, ws, stream)
+                else:
+                    lm.lmhead_logps_bwd(h, W, t, C, lse, ent, gl, ge, dh, dW, ws, stream)
+            time.sleep(2.0)
+            out["power"][kind] = smi_power()
+            torch.cuda.synchronize()
     real = int(np.count_nonzero((targets >= 0) & (targets < V)))
     if real != N:   # padded workloads: the rate of real (unmasked) tokens as well
         out["real_tokens_per_s"] = round(real * args.steps / elapsed, 1)
