@@ -292,8 +292,10 @@ int lmhead_logps_bwd_shard(const uint16_t* hidden, const uint16_t* W_shard, cons
  * on one GPU (several streams or threads at once) race and must not be made;
  * calls in stream order are safe (each call writes every record it reads).
  * The first call on a device looks the array's address up (set-up, no
- * allocation). Errors: as for lmhead_logps_fwd_temp, plus LMH_ERR_WORKSPACE
- * as above and LMH_ERR_HIP if the address lookup fails.
+ * allocation). With the library's tracing on (a measurement facility, off
+ * by default), every launch also records two HIP events, which the tracing
+ * creates on first use. Errors: as for lmhead_logps_fwd_temp, plus
+ * LMH_ERR_WORKSPACE as above and LMH_ERR_HIP if the address lookup fails.
  */
 #define LMH_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
 int lmhead_logps_fwd_noalloc(const uint16_t* hidden, const uint16_t* W, const int32_t* targets,
