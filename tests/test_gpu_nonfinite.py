@@ -154,3 +154,52 @@ def test_row_of_no_finite_logit_gradients():
     ref_dh, ref_dW = O.backward(hn, Wn, t, 64, g_l, None)
     _same_grad(got["dh"], ref_dh, "no finite logit dh")
     _same_grad(got["dW"], ref_dW, "no finite logit dW")
+
+
+@pytest.mark.parametrize("kind,bits", [("-inf", NEG_INF), ("+inf", POS_INF)])
+def test_nonfinite_gradients_tempered(kind, bits):
+    """The same readings at T = 0.7: the tempered cotangent divides by T,
+    which moves no NaN or inf and scales the finite values."""
+    h, W, t = _case(seed=45)
+    rng = np.random.default_rng(7)
+    valid = t >= 0
+    t[np.flatnonzero(valid)[:4]] = 100
+    g_l = rng.standard_normal(t.size).astype(np.float32)
+    g_e = (rng.standard_normal(t.size) * 0.1).astype(np.float32)
+    g_e[::3] = 0.0
+    Ws = _special_row(W, 100, bits)
+    log(f"[nonfinite] tempered gradients: {kind}")
+    got = run_head(h, Ws, t, 64, g_l, g_e, backward=True, temperature=0.7)
+    ref_dh, ref_dW = O.backward(h, Ws, t, 64, g_l, g_e, temperature=0.7)
+    assert np.all(got["dh"][~valid] == 0.0)
+    _same_grad(got["dh"], ref_dh, f"tempered {kind} dh")
+    _same_grad(got["dW"], ref_dW, f"tempered {kind} dW")
+
+
+@pytest.mark.parametrize("kind,bits", [("-inf", NEG_INF), ("NaN", NAN)])
+def test_nonfinite_bf16_gradients(kind, bits):
+    """The bf16-gradient backward at a non-finite entry: the same NaN and inf
+    positions as the float32 backward, and its finite values rounded to bf16."""
+    import torch
+    import cross_entropy_amd as lm
+    from gpu_common import dev, dev_bits
+    h, W, t = _case(seed=46)
+    rng = np.random.default_rng(8)
+    valid = t >= 0
+    t[np.flatnonzero(valid)[:4]] = 777
+    g_l = rng.standard_normal(t.size).astype(np.float32)
+    Ws = _special_row(W, 777, bits)
+    hd, Wd, td = dev_bits(h), dev_bits(Ws), dev(t)
+    logp, ent, lse = lm.forward(hd, Wd, td, 64)
+    log(f"[nonfinite] bf16 gradients: {kind}")
+    dh32, dW32 = lm.backward(hd, Wd, td, 64, lse, None, dev(g_l), None)
+    dh16, dW16 = lm.backward(hd, Wd, td, 64, lse, None, dev(g_l), None, grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for name, a32, a16 in (("dh", dh32, dh16), ("dW", dW32, dW16)):
+        f = a32.cpu().numpy()
+        b = a16.float().cpu().numpy()
+        assert np.array_equal(np.isnan(f), np.isnan(b)), f"{name}: NaN positions"
+        assert np.array_equal(np.isposinf(f), np.isposinf(b)) and np.array_equal(np.isneginf(f), np.isneginf(b))
+        fin = np.isfinite(f)
+        want = a32.to(torch.bfloat16).float().cpu().numpy()
+        assert np.array_equal(want[fin], b[fin]), f"{name}: finite values are not the float32 ones rounded"
