@@ -326,20 +326,35 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 
-// The current device's address of `scratch` (looked up on its first use there).
-int scratch_address(void** out) {
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
+// The address of `scratch` on the device the work runs on: the stream's
+// device (the current device for the NULL stream). Looked up once per device,
+// with that device current; the caller's current device is restored.
+int scratch_address(hipStream_t stream, void** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return fail(LMH_ERR_HIP, "fwd_noalloc: hipGetDevice failed: %s", hipGetErrorString(e));
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t sd = 0;
+    e = hipStreamGetDevice(stream, &sd);
+    if (e != hipSuccess)
+      return fail(LMH_ERR_HIP, "fwd_noalloc: hipStreamGetDevice failed: %s", hipGetErrorString(e));
+    dev = (int)sd;
+  }
   if (dev < 0 || dev >= kMaxDevices)
     return fail(LMH_ERR_UNSUPPORTED, "fwd_noalloc: device %d is beyond the %d the library tracks", dev, kMaxDevices);
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(LMH_ERR_HIP, "fwd_noalloc: hipSetDevice(%d) failed: %s", dev, hipGetErrorString(e));
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = dev != cur ? hipSetDevice(cur) : hipSuccess;
     if (e != hipSuccess || p == nullptr)
       return fail(LMH_ERR_HIP, "fwd_noalloc: hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
                   hipGetErrorString(e));
+    if (back != hipSuccess)
+      return fail(LMH_ERR_HIP, "fwd_noalloc: restoring device %d failed: %s", cur, hipGetErrorString(back));
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];
@@ -365,7 +380,7 @@ int lmhead_logps_fwd_noalloc(const uint16_t* hidden, const uint16_t* W, const in
                 "with a workspace)",
                 (long long)N, need, (size_t)LMH_NOALLOC_SCRATCH_BYTES);
   void* ws = nullptr;
-  rc = scratch_address(&ws);
+  rc = scratch_address(static_cast<hipStream_t>(stream), &ws);
   if (rc != LMH_OK) return rc;
   return fwd_impl("fwd_noalloc", hidden, W, targets, N, H, V, 0, V, chunk_size, temperature, logp, entropy, lse,
                   nullptr, ws, (size_t)LMH_NOALLOC_SCRATCH_BYTES, stream);

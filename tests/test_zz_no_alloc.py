@@ -60,6 +60,27 @@ def test_noalloc_forward_two_calls(T):
             assert np.all(a[~valid] == 0.0), f"noalloc masked {k}"
 
 
+def test_noalloc_forward_on_a_side_stream():
+    """On a stream of its own (the library takes the scratch of the stream's
+    device) the allocation-free forward gives the workspace forward's bits."""
+    import torch
+    import cross_entropy_amd as lm
+    h_bits, W_bits, t = _inputs(75, 2000, 256, 3001, 13)
+    h, W, tt = dev_bits(h_bits), dev_bits(W_bits), dev(t)
+    N = t.size
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    a = [torch.empty(N, device="cuda") for _ in range(3)]
+    b = [torch.empty(N, device="cuda") for _ in range(3)]
+    ws = lm.workspace_for(h, W, 256, with_backward=False)
+    with torch.cuda.stream(side):
+        lm.lmhead_logps_fwd_noalloc(h, W, tt, 256, 1.0, *a, stream=side)
+        lm.lmhead_logps_fwd_temp(h, W, tt, 256, 1.0, *b, ws, stream=side)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert np.array_equal(x.cpu().numpy().view(np.uint32), y.cpu().numpy().view(np.uint32))
+
+
 def test_noalloc_rejects_beyond_its_scratch():
     """A call whose partial records exceed the fixed array fails on the host
     with LMH_ERR_WORKSPACE and writes nothing."""
