@@ -106,5 +106,27 @@ def build(verbose: bool = False, sanitize: bool = False) -> str:
     return out
 
 
+CAPI_SRC = os.path.join(ROOT, "tests", "capi", "capi_check.cpp")
+CAPI_BIN = os.path.join(ROOT, "tests", "capi", "capi_check")
+
+
+def build_capi_check(verbose: bool = False) -> str:
+    """Compile tests/capi/capi_check.cpp, a caller of the C ABI with no Python
+    and no PyTorch, linked against the in-tree library (run by the GPU test
+    tests/test_gpu_capi.py). Needs the library built first."""
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build the library first")
+    tmp = CAPI_BIN + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-O2", "-std=c++17", "-Wall", CAPI_SRC, "-o", tmp,
+           "-L" + PKG, "-llmhead_logps", "-Wl,-rpath,$ORIGIN/../../cross_entropy_amd"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{proc.stderr}")
+    os.replace(tmp, CAPI_BIN)
+    return CAPI_BIN
+
+
 if __name__ == "__main__":
     print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:]))
