@@ -263,5 +263,8 @@ def test_tracing_counts_launches():
     assert tr["bwd_step_kernel"]["launches"] >= 2 and tr["transpose_kernel"]["launches"] == 1
     assert tr["pad_rows_kernel"]["launches"] == 1   # 1000 % 64 != 0: W's last rows are padded
     assert abs(tr["fwd_stats_kernel"]["flops"] - 2.0 * 300 * 128 * 1000) < 1.0
+    # the backward's credited work: the dh and dW GEMMs, 4 N H V over its launches (the
+    # logits recompute is executed, not counted); the bench's roofline.frac rests on it
+    assert abs(tr["bwd_step_kernel"]["flops"] - 4.0 * 300 * 128 * 1000) < 1.0
     assert tr["fwd_stats_kernel"]["ms"] > 0.0
     _ = lm
