@@ -88,10 +88,41 @@ def test_golden_bruteforce_case():
     (64, 64, 5, 1, 3),             # fewer vocabulary rows than one MFMA block
     (2048, 256, 20000, 512, 9),    # 27 forward splits of 3 chained vocabulary tiles; the last tile ragged
     (1, 128, 777, 1, 0),           # one token: one cotangent tile per launch, 7 XCDs with nothing to take
+    (129, 192, 2, 16, 4),          # two vocabulary rows
 ])
 def test_parity_full_small(N, H, V, C, n_masked):
     h, W, t, g_l, g_e = _case(N * 7 + V, N, H, V, n_masked=n_masked, masked_ids=(-1, V, -3))
     _check_full(h, W, t, C, g_l, g_e, f"small({N},{H},{V},{C})")
+
+
+def test_parity_one_vocabulary_row():
+    """V = 1: p = 1 for every token, so logp = entropy = 0, lse = z and both
+    gradients are exactly 0 in the oracle. The head's float32 arithmetic forms
+    log2 p as the difference of z log2(e) and lse log2(e), each rounded, so its
+    p is 1 only up to a few ulps of |z| and dz = g (1 - p) - g_ent p log p is
+    rounding noise. The relative Frobenius bar is undefined against an exact
+    zero; the gradients are instead bounded elementwise by that noise,
+    |dz_i| <= (|g_l,i| + |g_ent,i|) 2^-20 (1 + |z_i|), carried through the two
+    products."""
+    N, H, V, C = 37, 64, 1, 8
+    h, W, t, g_l, g_e = _case(4242, N, H, V, w_std=0.5, n_masked=2, masked_ids=(-1, 1))
+    log(f"[parity] one vocabulary row: N={N} H={H} C={C}")
+    got = run_head(h, W, t, C, g_l, g_e)
+    ref = O.forward_backward(h, W, t, C, g_l, g_e)
+    valid = (t >= 0) & (t < V)
+    assert np.all(ref["dh"] == 0.0) and np.all(ref["dW"] == 0.0)
+    for k in ("logp", "entropy", "lse"):
+        assert_stats_close(got[k][valid], ref[k][valid], f"V=1 {k}")
+        assert np.all(got[k][~valid] == 0.0), f"V=1 masked {k}"
+    hf = O.widen_bf16(h)
+    Wf = O.widen_bf16(W)
+    z = hf @ Wf[0]
+    dz_bound = np.where(valid, (np.abs(g_l) + np.abs(g_e)) * 2.0 ** -20 * (1.0 + np.abs(z)), 0.0)
+    dh_bound = dz_bound[:, None] * np.abs(Wf[0])[None, :]
+    dW_bound = dz_bound @ np.abs(hf)
+    assert np.all(got["dh"][~valid] == 0.0), "V=1 masked dh rows"
+    assert np.all(np.abs(got["dh"]) <= dh_bound), f"V=1 dh: max {np.abs(got['dh']).max():.3e}"
+    assert np.all(np.abs(got["dW"][0]) <= dW_bound), f"V=1 dW: max {np.abs(got['dW']).max():.3e}"
 
 
 def test_parity_tiny_workload_full():
