@@ -146,6 +146,9 @@ def main() -> int:
                     help="synthetic workload (default 3, the batch-16 x 4096 headline; the others are "
                          "the one-sequence head, the context-rank share and the pad-first packed row)")
     ap.add_argument("--chunk", type=int, default=0, help="chunk_size override (workload 4 runs 1024 and 4096)")
+    ap.add_argument("--grad-dtype", choices=("f32", "bf16"), default="f32",
+                    help="gradient outputs: float32 (lmhead_logps_bwd, the default) or bf16 "
+                         "(lmhead_logps_bwd_bf16: float32 sums in the workspace, rounded once)")
     ap.add_argument("--power", action="store_true",
                     help="also read board power and XCD clocks (amd-smi) while the forward alone, then the "
                          "backward alone, run back to back for a few seconds each")
@@ -192,14 +195,22 @@ def main() -> int:
     logp = torch.empty(N, dtype=torch.float32, device=dev)
     ent = torch.empty(N, dtype=torch.float32, device=dev)
     lse = torch.empty(N, dtype=torch.float32, device=dev)
-    dh = torch.empty((N, H), dtype=torch.float32, device=dev)
-    dW = torch.empty((V, H), dtype=torch.float32, device=dev)
-    ws = lm.workspace_for(h, W, C, with_backward=True)
+    bf16_grads = args.grad_dtype == "bf16"
+    gdt = torch.bfloat16 if bf16_grads else torch.float32
+    dh = torch.empty((N, H), dtype=gdt, device=dev)
+    dW = torch.empty((V, H), dtype=gdt, device=dev)
+    ws = lm.workspace_for(h, W, C, with_backward="bf16" if bf16_grads else True)
     stream = torch.cuda.current_stream(dev)
+
+    def backward():
+        if bf16_grads:
+            lm.lmhead_logps_bwd_bf16(h, W, t, C, 1.0, lse, ent, gl, ge, dh, dW, 0, ws, stream)
+        else:
+            lm.lmhead_logps_bwd(h, W, t, C, lse, ent, gl, ge, dh, dW, ws, stream)
 
     def step():
         lm.lmhead_logps_fwd(h, W, t, C, logp, ent, lse, ws, stream)
-        lm.lmhead_logps_bwd(h, W, t, C, lse, ent, gl, ge, dh, dW, ws, stream)
+        backward()
 
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -215,7 +226,7 @@ def main() -> int:
         e0.record(stream)
         lm.lmhead_logps_fwd(h, W, t, C, logp, ent, lse, ws, stream)
         e1.record(stream)
-        lm.lmhead_logps_bwd(h, W, t, C, lse, ent, gl, ge, dh, dW, ws, stream)
+        backward()
         e2.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -251,7 +262,7 @@ def main() -> int:
         achieved = dom["flops"] / max(1, dom["launches"]) / (avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
-        recompute = 2.0 * N * H * V * args.steps if dom_name == "bwd_step_kernel" else 0.0
+        recompute = 2.0 * N * H * V * args.steps if dom_name.startswith("bwd_step") else 0.0
         exe = (dom["flops"] + recompute) / (dom["ms"] * 1e-3) / 1e12
         roof["executed_achieved"] = round(exe, 1)
         roof["executed_frac"] = round(exe / PEAK_BF16_TFLOPS, 4)
@@ -279,7 +290,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": dict({"workload": cfg.name, "N": N, "H": H, "V": V, "chunk_size": C},
+        "config": dict({"workload": cfg.name, "N": N, "H": H, "V": V, "chunk_size": C,
+                        "grad_dtype": args.grad_dtype},
                        **({"batch": 16, "seq_len": 4096} if args.workload == 3 else {}),
                        parallelism="none (one GPU)"),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
@@ -308,7 +320,7 @@ def main() -> int:
                 if kind == "forward":
                     lm.lmhead_logps_fwd(h, W, t, C, logp, ent, lse, ws, stream)
                 else:
-                    lm.lmhead_logps_bwd(h, W, t, C, lse, ent, gl, ge, dh, dW, ws, stream)
+                    backward()
             time.sleep(2.0)
             out["power"][kind] = smi_power()
             torch.cuda.synchronize()
