@@ -293,9 +293,10 @@ int lmhead_logps_bwd_shard(const uint16_t* hidden, const uint16_t* W_shard, cons
  * calls in stream order are safe (each call writes every record it reads).
  * The work runs on the stream's device (the current device for the NULL
  * stream); the first call there looks the array's address up with that
- * device current and restores the caller's (set-up, no allocation). With the library's tracing on (a measurement facility, off
- * by default), every launch also records two HIP events, which the tracing
- * creates on first use. Errors: as for lmhead_logps_fwd_temp, plus
+ * device current and restores the caller's (set-up, no allocation). With
+ * the library's tracing on (a measurement facility, off by default), every
+ * launch also records two HIP events, which the tracing creates on first
+ * use. Errors: as for lmhead_logps_fwd_temp, plus
  * LMH_ERR_WORKSPACE as above and LMH_ERR_HIP if the address lookup fails.
  */
 #define LMH_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
