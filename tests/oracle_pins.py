@@ -506,6 +506,43 @@ def pin_nonfinite_gradients():
     dh, dW = O.backward(h, _row_only(W, v, _BF16_NAN), t, 3, g_l, g_e)
     assert np.all(np.isnan(dW)) and np.all(np.isnan(dh[live])) and np.all(dh[6] == 0.0)
 
+
+def pin_bruteforce_random():
+    """The 50-digit brute force on random tiny cases: shapes from one token,
+    one hidden unit and one vocabulary row up, every chunk size from 1 to past
+    N, masked ids -1 and V, temperatures below and above 1, and W scales up
+    to 2 (logits in the tens, peaked softmaxes); forward values and both
+    gradients."""
+    rng = np.random.default_rng(2024)
+    temps = ("1", "0.5", "0.7", "2")
+    for case in range(8):
+        N = int(rng.integers(1, 5))
+        H = int(rng.integers(1, 6))
+        V = int(rng.integers(1, 8))
+        C = int(rng.integers(1, N + 2))
+        T = temps[case % len(temps)]
+        w_std = float(rng.uniform(0.3, 2.0))
+        h = bf16(rng.standard_normal((N, H)))
+        W = bf16(rng.standard_normal((V, H)) * w_std)
+        t = rng.integers(0, V, size=N).astype(np.int32)
+        if N > 1:
+            t[int(rng.integers(0, N))] = (-1, V)[case % 2]
+        g_l = rng.standard_normal(N)
+        g_e = rng.standard_normal(N) * 0.3
+        what = f"random case {case} (N={N} H={H} V={V} C={C} T={T})"
+        logp, ent, lse = O.forward(h, W, t, C, temperature=float(T))
+        for i, (lp, en, ls) in enumerate(B.forward(h.tolist(), W.tolist(), t.tolist(), temperature=T)):
+            _close(logp[i], float(lp), 1e-12, 1e-14, what=f"{what} logp[{i}]")
+            _close(ent[i], float(en), 1e-12, 1e-14, what=f"{what} entropy[{i}]")
+            _close(lse[i], float(ls), 1e-12, 1e-14, what=f"{what} lse[{i}]")
+        dh, dW = O.backward(h, W, t, C, g_l, g_e, temperature=float(T))
+        rdh, rdW = B.gradients(h.tolist(), W.tolist(), t.tolist(), g_l, g_e, temperature=T)
+        rdh = np.array([[float(x) for x in row] for row in rdh])
+        rdW = np.array([[float(x) for x in row] for row in rdW])
+        _close(dh, rdh, 1e-10, 1e-12 * max(1e-300, np.abs(rdh).max()), what=f"{what} dh")
+        _close(dW, rdW, 1e-10, 1e-12 * max(1e-300, np.abs(rdW).max()), what=f"{what} dW")
+
+
 ALL_PINS = [
     pin_W_zero,
     pin_h_zero,
@@ -513,6 +550,7 @@ ALL_PINS = [
     pin_V2,
     pin_bruteforce_forward,
     pin_bruteforce_gradients,
+    pin_bruteforce_random,
     pin_fd_gradients,
     pin_normalisation,
     pin_shift_invariance,
