@@ -125,6 +125,37 @@ def test_parity_one_vocabulary_row():
     assert np.all(np.abs(got["dW"][0]) <= dW_bound), f"V=1 dW: max {np.abs(got['dW']).max():.3e}"
 
 
+def test_parity_random_shapes():
+    """A seeded sweep of shapes the fixed cases do not pick: tokens 1 to
+    1,200, H from 64 to 448 in steps of 64 (partial last H tiles), vocabulary
+    2 to 6,000 (ragged last tiles and W tails), chunk sizes from 1 to past N,
+    up to a third of the tokens masked (ids -1, V, -7), temperatures 0.7 to
+    1.3, with and without the entropy cotangent; every output against the
+    oracle."""
+    rng = np.random.default_rng(31337)
+    for case in range(16):
+        N = int(rng.integers(1, 1201))
+        H = 64 * int(rng.integers(1, 8))
+        V = int(rng.integers(2, 6001))
+        C = int(rng.integers(1, N + 101))
+        T = (1.0, 0.7, 1.3)[case % 3]
+        with_ent = case % 4 != 3
+        n_masked = int(rng.integers(0, N // 3 + 1))
+        h, W, t, g_l, g_e = _case(1000 + case, N, H, V, w_std=float(rng.uniform(0.02, 0.3)),
+                                  n_masked=n_masked, masked_ids=(-1, V, -7))
+        what = f"random {case}: N={N} H={H} V={V} C={C} T={T} entropy cotangent {with_ent}"
+        log(f"[parity] {what}")
+        got = run_head(h, W, t, C, g_l, g_e, entropy_grad=with_ent, temperature=T)
+        ref = O.forward_backward(h, W, t, C, g_l, g_e if with_ent else None, temperature=T)
+        valid = (t >= 0) & (t < V)
+        for k in ("logp", "entropy", "lse"):
+            assert_stats_close(got[k][valid], ref[k][valid], f"{what} {k}")
+            assert np.all(got[k][~valid] == 0.0), f"{what} masked {k}"
+        assert np.all(got["dh"][~valid] == 0.0), f"{what} masked dh rows"
+        assert_grad_close(got["dh"], ref["dh"], f"{what} dh")
+        assert_grad_close(got["dW"], ref["dW"], f"{what} dW")
+
+
 def test_parity_tiny_workload_full():
     """Workload 1 exactly as specified, full comparison."""
     cfg = WORKLOADS[1]
