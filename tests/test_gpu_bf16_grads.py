@@ -87,6 +87,31 @@ def test_bf16_gradients_are_the_float32_ones_rounded(N, H, V, C, n_masked, T, en
     assert np.all(dh16.float().cpu().numpy()[~valid] == 0.0), "masked dh rows"
 
 
+def test_bf16_gradients_random_shapes():
+    """A seeded sweep of shapes on both sides of N = V (so both block
+    orders), chunk sizes 1 to past N, temperatures, with and without the
+    entropy cotangent and the accumulate flags: the bf16 gradients are the
+    float32 ones rounded, bit for bit."""
+    rng = np.random.default_rng(8086)
+    for case in range(10):
+        N = int(rng.integers(1, 2500))
+        H = 64 * int(rng.integers(1, 6))
+        V = int(rng.integers(2, 3000))
+        C = int(rng.integers(1, N + 50))
+        T = (1.0, 0.7, 1.3)[case % 3]
+        ent = case % 4 != 3
+        h, W, t, g_l, g_e = _case(900 + case, N, H, V, n_masked=int(rng.integers(0, N // 4 + 1)))
+        prev = None
+        if case % 2:
+            prev = (f32_to_bf16_bits(rng.standard_normal((N, H)).astype(np.float32) * 1e-2),
+                    f32_to_bf16_bits(rng.standard_normal((V, H)).astype(np.float32) * 1e-2))
+        what = f"random {case}: N={N} H={H} V={V} C={C} T={T} entropy={ent} accumulate={prev is not None}"
+        log(f"[bf16] {what}")
+        dh32, dW32, dh16, dW16 = _both(h, W, t, C, g_l, g_e if ent else None, T, prev=prev)
+        _assert_rounded(dh32, dh16, f"{what} dh")
+        _assert_rounded(dW32, dW16, f"{what} dW")
+
+
 @pytest.mark.parametrize("N,H,V,C", [(700, 320, 3001, 7), (2100, 128, 777, 64), (300, 128, 1000, 4096)])
 def test_bf16_gradients_add_into_previous(N, H, V, C):
     """With the accumulate flags: the previous bf16 values, widened, start

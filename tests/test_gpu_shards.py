@@ -81,6 +81,40 @@ def test_sharded_head_matches_oracle(bounds, T):
     assert_grad_close(got["dW"], ref["dW"], "shards dW")
 
 
+def test_random_shard_splits():
+    """A seeded sweep: random shapes, 1 to 6 shards cut at random rows (a
+    shard may be a single row), temperatures 0.7 to 1.3, masked ids -1 and
+    V; the merged statistics and the per-shard gradients against the oracle
+    of the whole vocabulary."""
+    rng = np.random.default_rng(4711)
+    for case in range(8):
+        N = int(rng.integers(1, 900))
+        H = 64 * int(rng.integers(1, 6))
+        V = int(rng.integers(8, 5000))
+        C = int(rng.integers(1, N + 50))
+        P = int(rng.integers(1, 7))
+        cuts = sorted(set(int(x) for x in rng.integers(1, V, size=P - 1)))
+        if case == 0:
+            cuts = sorted(set(cuts + [1, V - 1]))   # one-row shards at both ends
+        bounds = [0] + cuts + [V]
+        T = (1.0, 0.7, 1.3)[case % 3]
+        h, W, t, g_l, g_e = _case(600 + case, N, H, V, w_std=float(rng.uniform(0.02, 0.2)),
+                                  n_masked=int(rng.integers(0, N // 4 + 1)))
+        if N > 1:
+            t[int(rng.integers(0, N))] = V      # out of the whole vocabulary: masked
+        what = f"random shards {case}: N={N} H={H} V={V} C={C} bounds={bounds} T={T}"
+        log(f"[shards] {what}")
+        got = run_sharded(h, W, t, C, bounds, g_l, g_e, T=T)
+        ref = O.forward_backward(h, W, t, C, g_l, g_e, temperature=T)
+        valid = (t >= 0) & (t < V)
+        for k in ("logp", "entropy", "lse"):
+            assert_stats_close(got[k][valid], ref[k][valid], f"{what} {k}")
+            assert np.all(got[k][~valid] == 0.0), f"{what} masked {k}"
+        assert np.all(got["dh"][~valid] == 0.0), f"{what} masked dh"
+        assert_grad_close(got["dh"], ref["dh"], f"{what} dh")
+        assert_grad_close(got["dW"], ref["dW"], f"{what} dW")
+
+
 def test_one_shard_is_the_whole_table_bit_for_bit():
     """One shard covering the vocabulary, merged alone, gives the plain
     forward's bits (the same split records and merge arithmetic)."""
