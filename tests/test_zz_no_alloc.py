@@ -60,6 +60,39 @@ def test_noalloc_forward_two_calls(T):
             assert np.all(a[~valid] == 0.0), f"noalloc masked {k}"
 
 
+def test_noalloc_forward_random_sequence():
+    """A seeded sequence of calls of random sizes (larger and smaller in
+    turn, with and without the entropy output, temperatures 0.7 to 1.3) on the
+    one scratch array: each gives the workspace forward's bits."""
+    import torch
+    import cross_entropy_amd as lm
+    rng = np.random.default_rng(2718)
+    for call in range(10):
+        N = int(rng.integers(1, 12000))
+        H = 64 * int(rng.integers(1, 6))
+        V = int(rng.integers(2, 9000))
+        C = int(rng.integers(1, N + 100))
+        T = (1.0, 0.7, 1.3)[call % 3]
+        with_ent = call % 3 != 2
+        log(f"[noalloc] call {call}: N={N} H={H} V={V} C={C} T={T} entropy={with_ent}")
+        h_bits, W_bits, t = _inputs(800 + call, N, H, V, int(rng.integers(0, N // 4 + 1)))
+        h, W, tt = dev_bits(h_bits), dev_bits(W_bits), dev(t)
+        outs = []
+        for kind in ("noalloc", "workspace"):
+            logp = torch.full((N,), 7.0, device="cuda")
+            ent = torch.full((N,), 7.0, device="cuda") if with_ent else None
+            lse = torch.full((N,), 7.0, device="cuda")
+            if kind == "noalloc":
+                lm.lmhead_logps_fwd_noalloc(h, W, tt, C, T, logp, ent, lse)
+            else:
+                ws = lm.workspace_for(h, W, C, with_backward=False)
+                lm.lmhead_logps_fwd_temp(h, W, tt, C, T, logp, ent, lse, ws)
+            torch.cuda.synchronize()
+            outs.append([x.cpu().numpy().view(np.uint32) for x in (logp, ent, lse) if x is not None])
+        for a, b in zip(*outs):
+            assert np.array_equal(a, b), f"call {call}: noalloc differs from fwd_temp"
+
+
 def test_noalloc_forward_on_a_side_stream():
     """On a stream of its own (the library takes the scratch of the stream's
     device) the allocation-free forward gives the workspace forward's bits."""
