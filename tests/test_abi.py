@@ -349,3 +349,41 @@ def test_planner_sweep_sizes():
                     dz = 4 * min(max(C * V, 256 * 320), n_pad * (v_pad + 128)) + 4 * 64 * max(n_pad, v_pad)
                     ht = 2 * h_pad * (n_pad + 128)
                     assert b <= max(f, dz + ht + 2 * 64 * H + 8 * 4 * 8192 * 64 + 4096), (N, H, V, C, b)
+
+
+def test_last_error_is_per_thread():
+    """Each thread reads its own call's message (the library keeps the last
+    error thread-local): threads failing with different arguments at the same
+    time, each checking the message names its own value; a successful call
+    clears the calling thread's message only."""
+    import ctypes
+    import threading
+    lib = nat.load()
+    errors = []
+    start = threading.Barrier(8)
+
+    def worker(k):
+        try:
+            start.wait()
+            out = ctypes.c_size_t(0)
+            for it in range(2000):
+                bad = -(1000 * k + it + 1)
+                rc = lib.lmhead_logps_workspace_bytes(bad, 64, 100, 4, 0, ctypes.byref(out))
+                msg = lib.lmhead_logps_last_error().decode()
+                if rc != -2 or f"got {bad}" not in msg:
+                    errors.append((k, it, rc, msg))
+                    return
+                if it % 100 == 99:
+                    assert lib.lmhead_logps_workspace_bytes(10, 64, 100, 4, 0, ctypes.byref(out)) == 0
+                    if lib.lmhead_logps_last_error().decode() != "":
+                        errors.append((k, it, "not cleared"))
+                        return
+        except Exception as e:   # reported below, from the main thread
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
