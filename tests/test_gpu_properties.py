@@ -154,6 +154,52 @@ def test_runs_on_a_non_default_stream_and_reuses_one_workspace():
         assert np.array_equal(v.cpu().numpy(), ref[k]), k
 
 
+def test_concurrent_calls_from_threads_on_their_own_streams():
+    """The library keeps no state between calls: four host threads, each
+    with its own stream and workspace, run forward + backward on different
+    inputs at the same time (their kernels interleave on the GPU); every
+    output equals the same call made alone, bit for bit."""
+    import threading
+    import torch
+    import cross_entropy_amd as lm
+    shapes = [(900, 256, 3001, 64), (1500, 128, 5000, 512), (333, 320, 777, 7), (2048, 192, 2500, 300)]
+    cases = [_case(40 + k, N, H, V, n_masked=N // 20) for k, (N, H, V, C) in enumerate(shapes)]
+    log("[props] four threads on four streams")
+    refs = [run_head(h, W, t, C, g_l, g_e) for (h, W, t, g_l, g_e), (_, _, _, C) in zip(cases, shapes)]
+    dev_in = [(dev_bits(h), dev_bits(W), dev(t), dev(g_l), dev(g_e)) for h, W, t, g_l, g_e in cases]
+    torch.cuda.synchronize()
+    outs = [None] * len(cases)
+    errors = []
+    start = threading.Barrier(len(cases))
+
+    def worker(k):
+        try:
+            hd, Wd, td, gl, ge = dev_in[k]
+            C = shapes[k][3]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                ws = lm.workspace_for(hd, Wd, C, with_backward=True)
+                start.wait()
+                for _ in range(3):
+                    logp, ent, lse = lm.forward(hd, Wd, td, C, workspace=ws, stream=s)
+                    dh, dW = lm.backward(hd, Wd, td, C, lse, ent, gl, ge, workspace=ws, stream=s)
+                s.synchronize()
+            outs[k] = {"logp": logp, "entropy": ent, "lse": lse, "dh": dh, "dW": dW}
+        except Exception as e:   # reported from the main thread
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(len(cases))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for k, (ref, got) in enumerate(zip(refs, outs)):
+        for name, v in got.items():
+            assert np.array_equal(v.cpu().numpy(), ref[name]), (k, name)
+
+
 def test_backward_twice_on_one_workspace():
     """The backward's per-launch tile counters live in the workspace and are
     reset by each call: a second backward on the same (now dirty) workspace
